@@ -1,0 +1,228 @@
+/*
+ * mad.h -- C ABI of the mask-aware dense attention library for MI355X (gfx950).
+ *
+ * The library computes single-GPU softmax attention forward and backward
+ * (bf16 Q/K/V, fp32 accumulation, output plus log-sum-exp) under the mask
+ * patterns catalogued by "Long-Context Attention Benchmark: From Kernel
+ * Efficiency to Distributed Context Parallelism" (LongCA-bench): 12 static
+ * patterns and 2 dynamic block-sparse patterns (section 2.1.1 "Input mask
+ * patterns"; the notes' key design 1).  Its input follows the benchmark's
+ * unified input representation (section 2.1 "Data preparation", section 2.2
+ * "Attention kernel"): variable-length sequences packed along one token axis,
+ * MHA/GQA head mapping, and a mask described as a list of
+ * (q_range, k_range, full | causal) slices.
+ *
+ * Conventions shared by every entry point
+ *   - Token layout is packed, batch 1: Q is [Tq, Hq, d], K and V are
+ *     [Tk, Hkv, d], with d contiguous.  Query head h reads KV head
+ *     h / (Hq / Hkv) (contiguous GQA groups; Hkv == Hq is MHA).
+ *   - Device pointers come from the caller (for example PyTorch tensors);
+ *     the library never frees them.  Host pointers are read during the call
+ *     only.  Kernels run on the caller's hipStream_t; a call returns after
+ *     enqueueing, so results are ready when the stream is.
+ *   - Every call validates its arguments before it writes or launches
+ *     anything.  On failure it returns a non-zero mad_status, writes and
+ *     launches nothing, and mad_last_error() returns a message for the
+ *     calling thread.  Faults inside a kernel surface at the caller's next
+ *     synchronisation of the stream.
+ *   - Floating point: inputs and O/dQ/dK/dV are bf16 (round to nearest
+ *     even on output); LSE and the delta workspace are fp32; LSE is the
+ *     natural log of the sum of exp(scale * q.k) over allowed keys.  A query
+ *     row with no allowed key gets O = 0 and LSE = -inf.
+ */
+#ifndef MAD_H_
+#define MAD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MAD_OK = 0,
+  MAD_ERR_INVALID = 1,     /* bad argument: null pointer, size, range, plan/shape mismatch */
+  MAD_ERR_UNSUPPORTED = 2, /* valid but not built: head dim other than 64/128, alignment */
+  MAD_ERR_HIP = 3,         /* a HIP runtime call failed (message holds the HIP error) */
+  MAD_ERR_NOMEM = 4        /* host or device allocation for plan metadata failed */
+} mad_status;
+
+/* ---------------------------------------------------------------------------
+ * Mask slices -- the unified mask description.
+ *
+ * A slice allows the pairs (i, j) with q0 <= i < q1 and k0 <= j < k1, and
+ *   FULL   : every pair of the rectangle;
+ *   CAUSAL : pairs with (j - k0) <= (i - q0), i.e. causal aligned at the
+ *            slice's top-left corner, and if window > 0 additionally
+ *            (i - q0) - (j - k0) < window (a causal sliding window that
+ *            counts the key itself).
+ * The mask is the union of all slices; slices may overlap.  Indices are
+ * global token positions in the packed Q (i) and K (j) streams.
+ * ------------------------------------------------------------------------- */
+enum { MAD_SLICE_FULL = 0, MAD_SLICE_CAUSAL = 1 };
+
+typedef struct {
+  int32_t q0, q1; /* half-open query range */
+  int32_t k0, k1; /* half-open key range */
+  int32_t type;   /* MAD_SLICE_FULL or MAD_SLICE_CAUSAL */
+  int32_t window; /* CAUSAL only: 0 = unbounded, W > 0 = W-key causal window */
+} mad_slice;
+
+/* ---------------------------------------------------------------------------
+ * Static mask patterns (LongCA-bench section 2.1.1; the notes' key design 1:
+ * six regular patterns -- FULL, CAUSAL, sliding window and the document
+ * variants -- and six heterogeneous ones -- Shared Question, Global Sliding,
+ * Causal Blockwise, Prefix LM, Block Causal Document and a sixth one the
+ * pages do not name, read here as Prefix LM applied per packed document).
+ * ------------------------------------------------------------------------- */
+typedef enum {
+  MAD_MASK_FULL = 0,
+  MAD_MASK_CAUSAL = 1,
+  MAD_MASK_SLIDING_WINDOW = 2,                 /* i - W < j <= i */
+  MAD_MASK_FULL_DOCUMENT = 3,                  /* same document */
+  MAD_MASK_CAUSAL_DOCUMENT = 4,                /* same document and j <= i */
+  MAD_MASK_SLIDING_WINDOW_CAUSAL_DOCUMENT = 5, /* same document and i - W < j <= i */
+  MAD_MASK_PREFIX_LM = 6,                      /* j <= max(i, P - 1) */
+  MAD_MASK_SHARED_QUESTION = 7,                /* causal; answers see the question and themselves */
+  MAD_MASK_GLOBAL_SLIDING = 8,                 /* j <= i and (j < G or i - j < W) */
+  MAD_MASK_CAUSAL_BLOCKWISE = 9,               /* causal in a block, full to earlier blocks */
+  MAD_MASK_BLOCK_CAUSAL_DOCUMENT = 10,         /* same document, block-causal from the doc start */
+  MAD_MASK_PREFIX_LM_DOCUMENT = 11             /* prefix LM inside each document, p = L/4 */
+} mad_mask_pattern;
+
+typedef struct {
+  int32_t window;          /* SLIDING_WINDOW*, GLOBAL_SLIDING: W (> 0) */
+  int32_t prefix;          /* PREFIX_LM: P; < 0 selects floor(T/4) */
+  int32_t question;        /* SHARED_QUESTION: question length */
+  int32_t n_answers;       /* SHARED_QUESTION: answers split the rest equally, the last takes the remainder */
+  int32_t global_len;      /* GLOBAL_SLIDING: G */
+  int32_t block;           /* CAUSAL_BLOCKWISE and BLOCK_CAUSAL_DOCUMENT block size (> 0) */
+  const int32_t* doc_lens; /* *_DOCUMENT: host array of n_docs lengths summing to T */
+  int32_t n_docs;
+} mad_mask_params;
+
+/* Build the slice list of a static pattern over a square T x T mask.
+ * out may be NULL to query the count; otherwise it must hold cap slices.
+ * *n_out receives the number of slices.  Host only; launches nothing. */
+mad_status mad_mask_slices(int32_t pattern, int32_t T, const mad_mask_params* params,
+                           mad_slice* out, int64_t cap, int64_t* n_out);
+
+/* One GPU's share of a context-parallel ring step (LongCA-bench section 2.3
+ * and the notes' key design 3).  The causal sequence of n_ranks * chunk tokens
+ * is split over n_ranks ranks; layout 0 = contiguous (rank r holds chunk r),
+ * layout 1 = head-tail (2 * n_ranks halves; rank r holds halves r and
+ * 2 * n_ranks - 1 - r, which balances causal work).  The slices describe which
+ * local queries of `rank` see which local keys received from rank `source`,
+ * in the two ranks' local coordinates.  chunk must be even for head-tail. */
+mad_status mad_ring_step_slices(int32_t layout, int32_t n_ranks, int32_t chunk, int32_t rank,
+                                int32_t source, mad_slice* out, int64_t cap, int64_t* n_out);
+
+/* Dynamic block-sparse masks (LongCA-bench appendix A.2: block partition,
+ * block scores, top-k key blocks per query block).  scores is a host array
+ * [n_groups][n_qb][n_kb] of fp32 block scores; for each (group, query block)
+ * the k = n_kb - floor(sparsity_pct * n_kb / 100) (at least 1) highest
+ * scoring key blocks are kept, equal scores preferring the lower block index.
+ * keep receives a host bitmap [n_groups][n_qb][ceil(n_kb / 64)] of uint64
+ * words, bit (kb % 64) of word kb / 64.  sparsity_pct is in [0, 100]. */
+mad_status mad_block_topk(const float* scores, int32_t n_groups, int32_t n_qb, int32_t n_kb,
+                          int32_t sparsity_pct, uint64_t* keep);
+
+/* ---------------------------------------------------------------------------
+ * Plans.  A plan is the compiled mask: for each kernel tiling it sorts every
+ * Q x K tile into EMPTY (skipped), FULL (no mask arithmetic) or PARTIAL
+ * (per-element mask), and holds per-query-tile lists of key tiles (used by
+ * the forward and dQ kernels) and per-key-tile lists of query tiles (used by
+ * the dK/dV kernel).  A tile is judged on its in-range elements only.  Plans
+ * are immutable after mad_plan_upload and may be shared across streams.
+ * ------------------------------------------------------------------------- */
+typedef struct mad_plan mad_plan;
+
+/* Compile n slices for a Tq x Tk mask.  Every slice must satisfy
+ * 0 <= q0 <= q1 <= Tq, 0 <= k0 <= k1 <= Tk, a known type and window >= 0.
+ * Host only: call mad_plan_upload before attention calls.  The plan is owned
+ * by the caller and released with mad_plan_destroy. */
+mad_status mad_mask_compile(const mad_slice* slices, int64_t n, int32_t Tq, int32_t Tk,
+                            mad_plan** out);
+
+/* Compile a block-sparse mask.  q_edges (n_qb + 1 entries) and k_edges
+ * (n_kb + 1) are strictly increasing block boundaries from 0 to Tq and Tk;
+ * keep is the bitmap of mad_block_topk for n_groups mask groups.  Query head
+ * h uses mask group h / (Hq / n_groups), so n_groups = Hkv shares one keep set
+ * per GQA group and n_groups = Hq (MHA) gives one per head.  Host only. */
+mad_status mad_sparse_plan(int32_t n_groups, const int32_t* q_edges, int32_t n_qb,
+                           const int32_t* k_edges, int32_t n_kb, const uint64_t* keep,
+                           mad_plan** out);
+
+/* Copy the plan's metadata to the current device (allocates device memory
+ * owned by the plan; synchronises `stream`).  Idempotent. */
+mad_status mad_plan_upload(mad_plan* plan, hipStream_t stream);
+
+/* Plan statistics.  pairs_per_group (n_groups entries, may be NULL) receives
+ * the exact number of allowed (i, j) pairs of each mask group;
+ * n_full/n_partial/n_empty (may be NULL) receive the tile-class counts of
+ * tiling `which` (0 = forward/dQ tiling, 1 = dK/dV tiling) summed over groups. */
+mad_status mad_plan_stats(const mad_plan* plan, int32_t which, int64_t* pairs_per_group,
+                          int64_t* n_full, int64_t* n_partial, int64_t* n_empty);
+
+/* Plan shape: Tq, Tk, number of mask groups, and tile sizes (BM query rows x
+ * BN keys) with tile-grid size of tiling `which`.  Any out pointer may be NULL. */
+mad_status mad_plan_info(const mad_plan* plan, int32_t which, int32_t* Tq, int32_t* Tk,
+                         int32_t* n_groups, int32_t* BM, int32_t* BN, int32_t* n_qt,
+                         int32_t* n_kt);
+
+/* Export tiling `which` for mask group `group` to host arrays:
+ * classes [n_qt * n_kt] (0 EMPTY, 1 FULL, 2 PARTIAL, row-major by query tile),
+ * csr_ptr [n_qt + 1] / csr_idx [entries] (ascending key tiles per query tile),
+ * csc_ptr [n_kt + 1] / csc_idx [entries] (ascending query tiles per key tile).
+ * Any output may be NULL; list lengths equal the number of non-EMPTY tiles. */
+mad_status mad_plan_export(const mad_plan* plan, int32_t which, int32_t group, uint8_t* classes,
+                           int64_t* csr_ptr, int32_t* csr_idx, int64_t* csc_ptr, int32_t* csc_idx);
+
+void mad_plan_destroy(mad_plan* plan);
+
+/* ---------------------------------------------------------------------------
+ * Attention.  strides (may be NULL = packed) gives, in elements, the token
+ * and head strides of q, k and v: {q_tok, q_head, k_tok, k_head, v_tok,
+ * v_head}; the head dimension must be contiguous and every row 16-byte
+ * aligned.  o, d_o, dq are packed [Tq, Hq, d]; dk, dv packed [Tk, Hkv, d];
+ * lse is [Hq, Tq].  d must be 64 or 128; Hq % Hkv == 0; the plan must have
+ * been compiled for (Tq, Tk), uploaded, and have n_groups dividing Hq.
+ * ------------------------------------------------------------------------- */
+
+/* Forward: O = softmax(scale * Q K^T + mask) V and LSE (LongCA-bench
+ * section 1: standard softmax attention).  Tiled with an online softmax;
+ * only non-EMPTY tiles are visited and only PARTIAL tiles evaluate the mask. */
+mad_status mad_attn_fwd(const mad_plan* plan, const void* q, const void* k, const void* v,
+                        void* o, float* lse, int32_t Tq, int32_t Tk, int32_t Hq, int32_t Hkv,
+                        int32_t d, const int64_t* strides, float scale, hipStream_t stream);
+
+/* Bytes of device workspace mad_attn_bwd needs (the delta rows, fp32 [Hq, Tq]). */
+mad_status mad_bwd_workspace_bytes(const mad_plan* plan, int32_t Tq, int32_t Tk, int32_t Hq,
+                                   int32_t Hkv, int32_t d, size_t* bytes);
+
+/* Backward of the forward above for upstream gradient d_o, given o and lse
+ * (normally the forward's; for a ring step the merged global ones, so the
+ * step's share of the global gradient is produced).  Runs the delta pre-pass
+ * D = rowsum(d_o * o) into the workspace, then the dK/dV kernel and the dQ
+ * kernel.  dq, dk, dv are overwritten.  workspace must be 256-byte aligned
+ * and at least mad_bwd_workspace_bytes long; q/k/v/o/d_o are not modified. */
+mad_status mad_attn_bwd(const mad_plan* plan, const void* q, const void* k, const void* v,
+                        const void* o, const void* d_o, const float* lse, void* dq, void* dk,
+                        void* dv, void* workspace, size_t workspace_bytes, int32_t Tq,
+                        int32_t Tk, int32_t Hq, int32_t Hkv, int32_t d, const int64_t* strides,
+                        float scale, hipStream_t stream);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* mad_last_error(void);
+
+/* Library version string. */
+const char* mad_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAD_H_ */

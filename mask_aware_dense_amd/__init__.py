@@ -1,0 +1,250 @@
+"""Python binding of libmad.so, the MI355X mask-aware attention library.
+
+Argument marshalling only: every function here converts Python / numpy /
+torch arguments to the C ABI declared in include/mad.h and calls it.  Mask
+generation, mask compilation and every attention step run in the library
+(host C++ and gfx950 HIP kernels).  PyTorch supplies device memory and the
+current HIP stream.  Importing this module never falls back to another
+implementation: if libmad.so is missing the import of the library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "MadError", "lib", "Plan", "mask_slices", "ring_step_slices", "block_topk",
+    "mask_compile", "sparse_plan", "attn_fwd", "attn_bwd", "bwd_workspace_bytes",
+    "PATTERNS", "SLICE_DTYPE",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmad.so")
+
+PATTERNS = {
+    "FULL": 0, "CAUSAL": 1, "SLIDING_WINDOW": 2, "FULL_DOCUMENT": 3, "CAUSAL_DOCUMENT": 4,
+    "SLIDING_WINDOW_CAUSAL_DOCUMENT": 5, "PREFIX_LM": 6, "SHARED_QUESTION": 7,
+    "GLOBAL_SLIDING": 8, "CAUSAL_BLOCKWISE": 9, "BLOCK_CAUSAL_DOCUMENT": 10,
+    "PREFIX_LM_DOCUMENT": 11,
+}
+
+SLICE_DTYPE = np.dtype([("q0", "<i4"), ("q1", "<i4"), ("k0", "<i4"), ("k1", "<i4"),
+                        ("type", "<i4"), ("window", "<i4")])
+
+
+class MadError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"mad status {status}: {msg}")
+        self.status = status
+
+
+class _Slice(ctypes.Structure):
+    _fields_ = [("q0", ctypes.c_int32), ("q1", ctypes.c_int32), ("k0", ctypes.c_int32),
+                ("k1", ctypes.c_int32), ("type", ctypes.c_int32), ("window", ctypes.c_int32)]
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int32), ("prefix", ctypes.c_int32), ("question", ctypes.c_int32),
+                ("n_answers", ctypes.c_int32), ("global_len", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("doc_lens", ctypes.POINTER(ctypes.c_int32)), ("n_docs", ctypes.c_int32)]
+
+
+_I32, _I64, _F32, _VP = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+_PI64 = ctypes.POINTER(ctypes.c_int64)
+_PI32 = ctypes.POINTER(ctypes.c_int32)
+
+_SIGS = {
+    "mad_mask_slices": (_I32, [_I32, _I32, ctypes.POINTER(_Params), _VP, _I64, _PI64]),
+    "mad_ring_step_slices": (_I32, [_I32, _I32, _I32, _I32, _I32, _VP, _I64, _PI64]),
+    "mad_block_topk": (_I32, [_VP, _I32, _I32, _I32, _I32, _VP]),
+    "mad_mask_compile": (_I32, [_VP, _I64, _I32, _I32, ctypes.POINTER(_VP)]),
+    "mad_sparse_plan": (_I32, [_I32, _VP, _I32, _VP, _I32, _VP, ctypes.POINTER(_VP)]),
+    "mad_plan_upload": (_I32, [_VP, _VP]),
+    "mad_plan_stats": (_I32, [_VP, _I32, _VP, _PI64, _PI64, _PI64]),
+    "mad_plan_info": (_I32, [_VP, _I32, _PI32, _PI32, _PI32, _PI32, _PI32, _PI32, _PI32]),
+    "mad_plan_export": (_I32, [_VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP]),
+    "mad_plan_destroy": (None, [_VP]),
+    "mad_attn_fwd": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP, _F32, _VP]),
+    "mad_bwd_workspace_bytes": (_I32, [_VP, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)]),
+    "mad_attn_bwd": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
+                            _I32, _I32, _I32, _I32, _I32, _VP, _F32, _VP]),
+    "mad_last_error": (ctypes.c_char_p, []),
+    "mad_version": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmad.so (built in-tree by mask_aware_dense_amd.build); raise if absent."""
+    global _lib
+    if _lib is None:
+        # torch first: its HIP runtime (libamdhip64.so.7) is then the one
+        # libmad.so binds to, so both share one runtime and one device context
+        import torch  # noqa: F401
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} not found: build it with `python -m mask_aware_dense_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise MadError(status, lib().mad_last_error().decode())
+
+
+def _ptr(a) -> int:
+    """Address of a numpy array's data, or of a torch tensor's storage."""
+    if a is None:
+        return None
+    if hasattr(a, "data_ptr"):
+        return a.data_ptr()
+    return a.ctypes.data
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+# --------------------------------------------------------------------------- masks
+
+def mask_slices(pattern, T: int, window: int = 4096, prefix: int = -1, question: int = 2048,
+                n_answers: int = 4, global_len: int = 256, block: int = 1024, doc_lens=None) -> np.ndarray:
+    """Slices (structured array of SLICE_DTYPE) of a static pattern over a T x T mask."""
+    pid = PATTERNS[pattern] if isinstance(pattern, str) else int(pattern)
+    docs = np.ascontiguousarray(np.asarray([] if doc_lens is None else doc_lens, dtype=np.int32))
+    prm = _Params(window, prefix, question, n_answers, global_len, block,
+                  docs.ctypes.data_as(_PI32) if docs.size else None, docs.size)
+    n = ctypes.c_int64(0)
+    _check(lib().mad_mask_slices(pid, T, ctypes.byref(prm), None, 0, ctypes.byref(n)))
+    out = np.zeros(n.value, dtype=SLICE_DTYPE)
+    _check(lib().mad_mask_slices(pid, T, ctypes.byref(prm), out.ctypes.data if n.value else None,
+                                 n.value, ctypes.byref(n)))
+    return out
+
+
+def ring_step_slices(layout, n_ranks: int, chunk: int, rank: int, source: int) -> np.ndarray:
+    """Slices of one ring step (layout "contiguous" or "headtail") in local coordinates."""
+    lid = {"contiguous": 0, "headtail": 1}[layout] if isinstance(layout, str) else int(layout)
+    n = ctypes.c_int64(0)
+    _check(lib().mad_ring_step_slices(lid, n_ranks, chunk, rank, source, None, 0, ctypes.byref(n)))
+    out = np.zeros(n.value, dtype=SLICE_DTYPE)
+    _check(lib().mad_ring_step_slices(lid, n_ranks, chunk, rank, source,
+                                      out.ctypes.data if n.value else None, n.value, ctypes.byref(n)))
+    return out
+
+
+def block_topk(scores: np.ndarray, sparsity_pct: int) -> np.ndarray:
+    """Keep bitmap uint64 [G, n_qb, ceil(n_kb/64)] of the top-k key blocks per query block."""
+    s = np.ascontiguousarray(scores, dtype=np.float32)
+    G, nq, nk = s.shape
+    keep = np.zeros((G, nq, (nk + 63) // 64), dtype=np.uint64)
+    _check(lib().mad_block_topk(s.ctypes.data, G, nq, nk, int(sparsity_pct), keep.ctypes.data))
+    return keep
+
+
+class Plan:
+    """Owner of a compiled mask (mad_plan*)."""
+
+    def __init__(self, handle):
+        self.handle = handle
+
+    def __del__(self):
+        h, self.handle = getattr(self, "handle", None), None
+        if h and _lib is not None:
+            _lib.mad_plan_destroy(h)
+
+    def upload(self, stream=None) -> "Plan":
+        _check(lib().mad_plan_upload(self.handle, _stream(stream)))
+        return self
+
+    def info(self, which: int = 0) -> dict:
+        v = [ctypes.c_int32() for _ in range(7)]
+        _check(lib().mad_plan_info(self.handle, which, *[ctypes.byref(x) for x in v]))
+        return dict(zip(("Tq", "Tk", "n_groups", "BM", "BN", "n_qt", "n_kt"), (x.value for x in v)))
+
+    def stats(self, which: int = 0) -> dict:
+        G = self.info(which)["n_groups"]
+        pairs = np.zeros(G, dtype=np.int64)
+        f, p, e = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().mad_plan_stats(self.handle, which, pairs.ctypes.data, ctypes.byref(f),
+                                    ctypes.byref(p), ctypes.byref(e)))
+        return {"pairs": pairs, "full": f.value, "partial": p.value, "empty": e.value}
+
+    def export(self, which: int = 0, group: int = 0) -> dict:
+        inf = self.info(which)
+        nq, nk = inf["n_qt"], inf["n_kt"]
+        cls = np.zeros(nq * nk, dtype=np.uint8)
+        csr_ptr = np.zeros(nq + 1, dtype=np.int64)
+        csc_ptr = np.zeros(nk + 1, dtype=np.int64)
+        _check(lib().mad_plan_export(self.handle, which, group, cls.ctypes.data, csr_ptr.ctypes.data,
+                                     None, csc_ptr.ctypes.data, None))
+        csr_idx = np.zeros(max(int(csr_ptr[-1]), 1), dtype=np.int32)
+        csc_idx = np.zeros(max(int(csc_ptr[-1]), 1), dtype=np.int32)
+        _check(lib().mad_plan_export(self.handle, which, group, None, None, csr_idx.ctypes.data,
+                                     None, csc_idx.ctypes.data))
+        return {"classes": cls.reshape(nq, nk), "csr_ptr": csr_ptr, "csr_idx": csr_idx[:csr_ptr[-1]],
+                "csc_ptr": csc_ptr, "csc_idx": csc_idx[:csc_ptr[-1]]}
+
+
+def mask_compile(slices: np.ndarray, Tq: int, Tk: int) -> Plan:
+    s = np.ascontiguousarray(slices, dtype=SLICE_DTYPE)
+    h = ctypes.c_void_p()
+    _check(lib().mad_mask_compile(s.ctypes.data if s.size else None, s.size, Tq, Tk, ctypes.byref(h)))
+    return Plan(h.value)
+
+
+def sparse_plan(n_groups: int, q_edges, k_edges, keep: np.ndarray) -> Plan:
+    qe = np.ascontiguousarray(q_edges, dtype=np.int32)
+    ke = np.ascontiguousarray(k_edges, dtype=np.int32)
+    kp = np.ascontiguousarray(keep, dtype=np.uint64)
+    h = ctypes.c_void_p()
+    _check(lib().mad_sparse_plan(n_groups, qe.ctypes.data, qe.size - 1, ke.ctypes.data, ke.size - 1,
+                                 kp.ctypes.data, ctypes.byref(h)))
+    return Plan(h.value)
+
+
+# --------------------------------------------------------------------------- attention
+
+def _qkv_strides(q, k, v):
+    arr = (ctypes.c_int64 * 6)(q.stride(0), q.stride(1), k.stride(0), k.stride(1), v.stride(0), v.stride(1))
+    for t in (q, k, v):
+        if t.stride(2) != 1:
+            raise MadError(2, "head dimension must be contiguous")
+    return arr
+
+
+def attn_fwd(plan: Plan, q, k, v, o, lse, scale: float, stream=None):
+    """Forward into preallocated o [Tq,Hq,d] bf16 and lse [Hq,Tq] fp32 (torch CUDA tensors)."""
+    Tq, Hq, d = q.shape
+    Tk, Hkv, _ = k.shape
+    st = _qkv_strides(q, k, v)
+    _check(lib().mad_attn_fwd(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), Tq, Tk, Hq, Hkv, d,
+                              st, float(scale), _stream(stream)))
+
+
+def bwd_workspace_bytes(plan: Plan, Tq: int, Tk: int, Hq: int, Hkv: int, d: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().mad_bwd_workspace_bytes(plan.handle, Tq, Tk, Hq, Hkv, d, ctypes.byref(n)))
+    return n.value
+
+
+def attn_bwd(plan: Plan, q, k, v, o, d_o, lse, dq, dk, dv, workspace, scale: float, stream=None):
+    """Backward into preallocated dq, dk, dv; workspace is a device buffer (uint8 tensor)."""
+    Tq, Hq, d = q.shape
+    Tk, Hkv, _ = k.shape
+    st = _qkv_strides(q, k, v)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().mad_attn_bwd(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
+                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes, Tq, Tk, Hq, Hkv, d,
+                              st, float(scale), _stream(stream)))

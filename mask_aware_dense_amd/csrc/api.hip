@@ -1,0 +1,265 @@
+// api.hip -- C ABI entry points for attention, plan upload and error reporting.
+//
+// Every entry point validates all arguments before it launches or writes
+// anything, returns a mad_status, and records a message for mad_last_error()
+// on the calling thread.  Kernels run on the caller's stream.
+#include <cstring>
+#include <string>
+
+#include "kernel_common.hpp"
+
+namespace mad {
+
+static thread_local std::string g_err;
+
+mad_status fail(mad_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+void clear_error() { g_err.clear(); }
+
+hipError_t launch_fwd(const AttnParams& P, int D, int n_items, hipStream_t stream);
+hipError_t launch_bwd(const AttnParams& Pq, const AttnParams& Pkv, int D, int nq_items, int nkv_items,
+                      hipStream_t stream);
+
+namespace {
+
+mad_status hip_fail(const char* where, hipError_t e) {
+  return fail(MAD_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Strides {
+  int64_t q_tok, q_head, k_tok, k_head, v_tok, v_head;
+};
+
+// Shared validation of the attention calls.
+mad_status check_common(const char* fn, const mad_plan* p, const void* q, const void* k, const void* v, int32_t Tq,
+                        int32_t Tk, int32_t Hq, int32_t Hkv, int32_t d, const int64_t* strides, Strides& st) {
+  const std::string f(fn);
+  if (!p) return fail(MAD_ERR_INVALID, f + ": plan is NULL");
+  if (Tq < 0 || Tk < 0 || Hq <= 0 || Hkv <= 0) return fail(MAD_ERR_INVALID, f + ": sizes must be Tq,Tk >= 0 and Hq,Hkv > 0");
+  if (Hq % Hkv) return fail(MAD_ERR_INVALID, f + ": Hq must be a multiple of Hkv");
+  if (d != 64 && d != 128) return fail(MAD_ERR_UNSUPPORTED, f + ": head dim must be 64 or 128");
+  if (p->Tq != Tq || p->Tk != Tk)
+    return fail(MAD_ERR_INVALID, f + ": plan was compiled for Tq=" + std::to_string(p->Tq) + ", Tk=" +
+                                     std::to_string(p->Tk));
+  if (Hq % p->G) return fail(MAD_ERR_INVALID, f + ": plan mask groups must divide Hq");
+  if (!p->dev_mem) return fail(MAD_ERR_INVALID, f + ": plan not uploaded (call mad_plan_upload)");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  if (dev != p->dev_id) return fail(MAD_ERR_INVALID, f + ": plan was uploaded to another device");
+  if (strides) {
+    st = Strides{strides[0], strides[1], strides[2], strides[3], strides[4], strides[5]};
+  } else {
+    st = Strides{(int64_t)Hq * d, d, (int64_t)Hkv * d, d, (int64_t)Hkv * d, d};
+  }
+  const int64_t all[6] = {st.q_tok, st.q_head, st.k_tok, st.k_head, st.v_tok, st.v_head};
+  for (int x = 0; x < 6; ++x)
+    if (all[x] < 0 || all[x] % 8) return fail(MAD_ERR_UNSUPPORTED, f + ": strides must be >= 0 and multiples of 8 elements");
+  if (Tq > 0 && Tk > 0 && (!q || !k || !v)) return fail(MAD_ERR_INVALID, f + ": q/k/v must not be NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return fail(MAD_ERR_UNSUPPORTED, f + ": q/k/v must be 16-byte aligned");
+  return MAD_OK;
+}
+
+AttnParams base_params(const mad_plan* p, int which, const void* q, const void* k, const void* v, int32_t Tq,
+                       int32_t Tk, int32_t Hq, int32_t Hkv, const Strides& st, float scale) {
+  AttnParams P;
+  std::memset(&P, 0, sizeof(P));
+  P.q = (const bf16*)q;
+  P.k = (const bf16*)k;
+  P.v = (const bf16*)v;
+  P.q_tok = st.q_tok;
+  P.q_head = st.q_head;
+  P.k_tok = st.k_tok;
+  P.k_head = st.k_head;
+  P.v_tok = st.v_tok;
+  P.v_head = st.v_head;
+  P.Tq = Tq;
+  P.Tk = Tk;
+  P.Hq = Hq;
+  P.Hkv = Hkv;
+  P.R = Hq / Hkv;
+  P.grp_div = Hq / p->G;
+  P.scale = scale;
+  P.scale_log2 = scale * LOG2E;
+  P.t = p->tdev[which];
+  P.m = p->mdev;
+  return P;
+}
+
+}  // namespace
+}  // namespace mad
+
+using namespace mad;
+
+extern "C" const char* mad_last_error(void) { return g_err.c_str(); }
+
+extern "C" const char* mad_version(void) { return "mask_aware_dense_amd 0.1 (gfx950)"; }
+
+extern "C" mad_status mad_plan_upload(mad_plan* p, hipStream_t stream) {
+  clear_error();
+  if (!p) return fail(MAD_ERR_INVALID, "mad_plan_upload: plan is NULL");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("mad_plan_upload", e);
+  if (p->dev_mem) {
+    if (dev == p->dev_id) return MAD_OK;
+    return fail(MAD_ERR_UNSUPPORTED, "mad_plan_upload: plan already uploaded to another device");
+  }
+  // Lay out every array in one allocation, 256-byte aligned pieces.
+  struct Piece {
+    const void* src;
+    size_t bytes;
+    size_t off;
+  };
+  std::vector<Piece> pieces;
+  size_t total = 0;
+  auto add = [&](const void* src, size_t bytes) -> size_t {
+    const size_t off = total;
+    pieces.push_back({src, bytes, off});
+    total += (bytes + 255) & ~(size_t)255;
+    return off;
+  };
+  size_t off_t[2][4];
+  for (int w = 0; w < 2; ++w) {
+    const TilingHost& t = p->tiling[w];
+    off_t[w][0] = add(t.ptr.data(), t.ptr.size() * 4);
+    off_t[w][1] = add(t.ent.data(), t.ent.size() * 4);
+    off_t[w][2] = add(t.ent_aux.data(), t.ent_aux.size() * 4);
+    off_t[w][3] = add(t.order.data(), t.order.size() * 4);
+  }
+  const size_t off_sl = add(p->slices.data(), p->slices.size() * sizeof(mad_slice));
+  const size_t off_ts = add(p->tile_slices.data(), p->tile_slices.size() * 4);
+  const size_t off_rq = add(p->row_qb.data(), p->row_qb.size() * 4);
+  const size_t off_ck = add(p->col_kb.data(), p->col_kb.size() * 4);
+  const size_t off_ke = add(p->k_edges.data(), p->k_edges.size() * 4);
+  const size_t off_kp = add(p->keep.data(), p->keep.size() * 8);
+  if (total == 0) total = 256;
+  void* mem = nullptr;
+  e = hipMalloc(&mem, total);
+  if (e != hipSuccess) return fail(MAD_ERR_NOMEM, std::string("mad_plan_upload: hipMalloc: ") + hipGetErrorString(e));
+  for (const Piece& pc : pieces) {
+    if (!pc.bytes) continue;
+    e = hipMemcpyAsync((char*)mem + pc.off, pc.src, pc.bytes, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) {
+      (void)hipFree(mem);
+      return hip_fail("mad_plan_upload: hipMemcpyAsync", e);
+    }
+  }
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) {
+    (void)hipFree(mem);
+    return hip_fail("mad_plan_upload: hipStreamSynchronize", e);
+  }
+  char* base = (char*)mem;
+  for (int w = 0; w < 2; ++w) {
+    const TilingHost& t = p->tiling[w];
+    TilingDev& d = p->tdev[w];
+    d.ptr = (const int32_t*)(base + off_t[w][0]);
+    d.ent = (const int32_t*)(base + off_t[w][1]);
+    d.ent_aux = (const int32_t*)(base + off_t[w][2]);
+    d.order = (const int32_t*)(base + off_t[w][3]);
+    d.nmajor = w == 0 ? t.nqt : t.nkt;
+    d.nminor = w == 0 ? t.nkt : t.nqt;
+  }
+  MaskDev& m = p->mdev;
+  m.mode = p->mode;
+  m.Tq = p->Tq;
+  m.Tk = p->Tk;
+  m.slices = (const mad_slice*)(base + off_sl);
+  m.tile_slices = (const int32_t*)(base + off_ts);
+  m.row_qb = (const int32_t*)(base + off_rq);
+  m.col_kb = (const int32_t*)(base + off_ck);
+  m.k_edges = (const int32_t*)(base + off_ke);
+  m.keep = (const uint64_t*)(base + off_kp);
+  m.n_qb = p->n_qb;
+  m.n_kb = p->n_kb;
+  m.nw = p->nw;
+  p->dev_mem = mem;
+  p->dev_id = dev;
+  return MAD_OK;
+}
+
+extern "C" void mad_plan_destroy(mad_plan* p) {
+  if (!p) return;
+  if (p->dev_mem) {
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (cur != p->dev_id) (void)hipSetDevice(p->dev_id);
+    (void)hipFree(p->dev_mem);
+    if (cur != p->dev_id && cur >= 0) (void)hipSetDevice(cur);
+  }
+  delete p;
+}
+
+extern "C" mad_status mad_attn_fwd(const mad_plan* p, const void* q, const void* k, const void* v, void* o, float* lse,
+                                   int32_t Tq, int32_t Tk, int32_t Hq, int32_t Hkv, int32_t d, const int64_t* strides,
+                                   float scale, hipStream_t stream) {
+  clear_error();
+  Strides st;
+  mad_status s = check_common("mad_attn_fwd", p, q, k, v, Tq, Tk, Hq, Hkv, d, strides, st);
+  if (s != MAD_OK) return s;
+  if (Tq > 0 && (!o || !lse)) return fail(MAD_ERR_INVALID, "mad_attn_fwd: o/lse must not be NULL");
+  if (!aligned16(o) || ((uintptr_t)lse & 3u)) return fail(MAD_ERR_UNSUPPORTED, "mad_attn_fwd: o must be 16-byte and lse 4-byte aligned");
+  if (!(scale == scale)) return fail(MAD_ERR_INVALID, "mad_attn_fwd: scale is NaN");
+  if (Tq == 0) return MAD_OK;
+  AttnParams P = base_params(p, 0, q, k, v, Tq, Tk, Hq, Hkv, st, scale);
+  P.o = (bf16*)o;
+  P.lse = lse;
+  const int64_t n_items = (int64_t)p->tiling[0].nqt * Hq;
+  if (n_items > INT32_MAX) return fail(MAD_ERR_UNSUPPORTED, "mad_attn_fwd: too many work items");
+  hipError_t e = launch_fwd(P, d, (int)n_items, stream);
+  if (e != hipSuccess) return hip_fail("mad_attn_fwd: launch", e);
+  return MAD_OK;
+}
+
+extern "C" mad_status mad_bwd_workspace_bytes(const mad_plan* p, int32_t Tq, int32_t Tk, int32_t Hq, int32_t Hkv,
+                                              int32_t d, size_t* bytes) {
+  clear_error();
+  if (!bytes) return fail(MAD_ERR_INVALID, "mad_bwd_workspace_bytes: bytes is NULL");
+  if (!p) return fail(MAD_ERR_INVALID, "mad_bwd_workspace_bytes: plan is NULL");
+  if (Tq < 0 || Tk < 0 || Hq <= 0 || Hkv <= 0) return fail(MAD_ERR_INVALID, "mad_bwd_workspace_bytes: bad sizes");
+  if (d != 64 && d != 128) return fail(MAD_ERR_UNSUPPORTED, "mad_bwd_workspace_bytes: head dim must be 64 or 128");
+  *bytes = (((size_t)Hq * (size_t)Tq * 4) + 255) & ~(size_t)255;
+  return MAD_OK;
+}
+
+extern "C" mad_status mad_attn_bwd(const mad_plan* p, const void* q, const void* k, const void* v, const void* o,
+                                   const void* d_o, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                                   size_t ws_bytes, int32_t Tq, int32_t Tk, int32_t Hq, int32_t Hkv, int32_t d,
+                                   const int64_t* strides, float scale, hipStream_t stream) {
+  clear_error();
+  Strides st;
+  mad_status s = check_common("mad_attn_bwd", p, q, k, v, Tq, Tk, Hq, Hkv, d, strides, st);
+  if (s != MAD_OK) return s;
+  if (Tq > 0 && (!o || !d_o || !lse || !dq)) return fail(MAD_ERR_INVALID, "mad_attn_bwd: o/d_o/lse/dq must not be NULL");
+  if (Tk > 0 && (!dk || !dv)) return fail(MAD_ERR_INVALID, "mad_attn_bwd: dk/dv must not be NULL");
+  if (!aligned16(o) || !aligned16(d_o) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3u))
+    return fail(MAD_ERR_UNSUPPORTED, "mad_attn_bwd: o/d_o/dq/dk/dv must be 16-byte and lse 4-byte aligned");
+  size_t need = 0;
+  mad_bwd_workspace_bytes(p, Tq, Tk, Hq, Hkv, d, &need);
+  if (Tq > 0 && (!workspace || ws_bytes < need))
+    return fail(MAD_ERR_INVALID, "mad_attn_bwd: workspace must hold " + std::to_string(need) + " bytes");
+  if ((uintptr_t)workspace & 255u) return fail(MAD_ERR_UNSUPPORTED, "mad_attn_bwd: workspace must be 256-byte aligned");
+  if (!(scale == scale)) return fail(MAD_ERR_INVALID, "mad_attn_bwd: scale is NaN");
+  if (Tq == 0 && Tk == 0) return MAD_OK;
+  AttnParams Pq = base_params(p, 0, q, k, v, Tq, Tk, Hq, Hkv, st, scale);
+  Pq.o_in = (const bf16*)o;
+  Pq.d_o = (const bf16*)d_o;
+  Pq.lse_in = lse;
+  Pq.delta = (float*)workspace;
+  Pq.dq = (bf16*)dq;
+  Pq.dk = (bf16*)dk;
+  Pq.dv = (bf16*)dv;
+  AttnParams Pkv = Pq;
+  Pkv.t = p->tdev[1];
+  const int64_t nq = Tq > 0 ? (int64_t)p->tiling[0].nqt * Hq : 0;
+  const int64_t nkv = Tk > 0 ? (int64_t)p->tiling[1].nkt * Hkv : 0;
+  if (nq > INT32_MAX || nkv > INT32_MAX) return fail(MAD_ERR_UNSUPPORTED, "mad_attn_bwd: too many work items");
+  hipError_t e = launch_bwd(Pq, Pkv, d, (int)nq, (int)nkv, stream);
+  if (e != hipSuccess) return hip_fail("mad_attn_bwd: launch", e);
+  return MAD_OK;
+}

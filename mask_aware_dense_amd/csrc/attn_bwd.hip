@@ -1,0 +1,392 @@
+// attn_bwd.hip -- backward attention kernels for gfx950.
+//
+// Gradients of the forward in attn_fwd.hip for upstream gradient dO, given
+// the forward's O and LSE (or merged ones for a ring step):
+//   P_ij  = exp(scale * q_i.k_j - LSE_i) on allowed (i, j), else 0
+//   D_i   = dO_i . O_i                              (delta pre-pass)
+//   dS_ij = P_ij (dO_i . v_j - D_i)
+//   dQ_i  = scale * sum_j dS_ij k_j                 (dQ kernel)
+//   dK_j  = scale * sum_{h in group} sum_i dS_ij q_i,  dV_j = sum_{h in group} sum_i P_ij dO_i   (dK/dV kernel)
+// The pages single out the backward pass as the common bottleneck (section
+// 3.2, the notes' key findings).  Here it is split into three launches with
+// no atomics: a streaming delta pre-pass, a dK/dV kernel that owns a key
+// tile and walks the query tiles of its per-key-tile list for every query
+// head of its GQA group, and a dQ kernel that owns a query tile and walks its
+// key-tile list (the forward's tiling).  Both recompute P from LSE.
+#include "kernel_common.hpp"
+
+namespace mad {
+
+// ---------------------------------------------------------------------------
+// Delta pre-pass: D[h][i] = sum_c dO[i][h][c] * O[i][h][c] (fp32).
+// One group of D/8 lanes per (row, head); inputs packed [Tq, Hq, D].
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void delta_kernel(const AttnParams P) {
+  constexpr int LPR = D / 8;  // lanes per row
+  const int64_t nrows = (int64_t)P.Tq * P.Hq;
+  const int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;
+  const int sub = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (r < nrows) {
+    const bf16x8 a = ld16(P.o_in + r * D + 8 * sub);
+    const bf16x8 b = ld16(P.d_o + r * D + 8 * sub);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+  if (r < nrows && sub == 0) {
+    const int64_t i = r / P.Hq, h = r % P.Hq;
+    P.delta[h * P.Tq + i] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ kernel: one workgroup per (query head, 128-row query tile), two waves of
+// 64 rows, walking the forward tiling's key-tile list.  Per key tile:
+//   S^T = K Q^T, dP^T = V dO^T       (keys x queries; lane = query row)
+//   P^T = exp2(S^T scale log2e - LSE log2e), dS^T = P^T (dP^T - D)
+//   dQ^T += K^T dS^T                 (K^T read transposed from LDS)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
+  constexpr int BM = BM0, BN = BN0, ST = lds_stride<D>(), NKS = D / 16, NDB = D / 32;
+  constexpr int CPR = D / 8, CH = BN * CPR / 128;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[BN * ST];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[BN * ST];
+
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int e = L % P.R, t_ = L / P.R;
+  const int g = t_ % P.Hkv, rank = t_ / P.Hkv;
+  const int h = g * P.R + e;
+  const int qt = P.t.order[rank];
+  const int mg = h / P.grp_div;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, li = lane & 31;
+  const int row_base = qt * BM + w * 64;
+
+  bf16x8 qf[2][NKS], df[2][NKS];
+  float lse2[2], dlt[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int row = row_base + b * 32 + li;
+    const bool in = row < P.Tq;
+    const bf16* qs = P.q + (int64_t)row * P.q_tok + (int64_t)h * P.q_head + 8 * hh;
+    const bf16* ds = P.d_o + ((int64_t)row * P.Hq + h) * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      qf[b][ks] = in ? ld16(qs + 16 * ks) : bf16x8{};
+      df[b][ks] = in ? ld16(ds + 16 * ks) : bf16x8{};
+    }
+    const float l = in ? P.lse_in[(int64_t)h * P.Tq + row] : -INFINITY;
+    // rows with no allowed key (LSE = -inf) and rows past Tq get P = 0
+    lse2[b] = (l == -INFINITY) ? INFINITY : l * LOG2E;
+    dlt[b] = in ? P.delta[(int64_t)h * P.Tq + row] : 0.f;
+  }
+
+  f32x16 acc[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[db][b] = f32x16{};
+
+  const int32_t* ptr = P.t.ptr + (int64_t)mg * (P.t.nmajor + 1);
+  const int beg = ptr[qt], end = ptr[qt + 1];
+
+  for (int it = beg; it < end; ++it) {
+    const uint32_t ent = (uint32_t)P.t.ent[it];
+    const int kt = (int)(ent & 0x7fffffffu);
+    const bool partial = (ent & ENT_PARTIAL) != 0;
+    u32x4 kr[CH], vr[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int id = tid + 128 * c, row = id / CPR, col = (id % CPR) * 8;
+      const int key = kt * BN + row;
+      if (key < P.Tk) {
+        kr[c] = gld16(P.k + (int64_t)key * P.k_tok + (int64_t)g * P.k_head + col);
+        vr[c] = gld16(P.v + (int64_t)key * P.v_tok + (int64_t)g * P.v_head + col);
+      } else {
+        kr[c] = u32x4{};
+        vr[c] = u32x4{};
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int id = tid + 128 * c, row = id / CPR, col = (id % CPR) * 8;
+      const int prow = (row & 32) | swap23(row & 31);
+      st16(Ks + prow * ST + col, kr[c]);
+      st16(Vs + prow * ST + col, vr[c]);
+    }
+    __syncthreads();
+
+    f32x16 s[2][2], dp[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        s[kb][b] = f32x16{};
+        dp[kb][b] = f32x16{};
+      }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 ak = ld16(Ks + (kb * 32 + li) * ST + 16 * ks + 8 * hh);
+        const bf16x8 av = ld16(Vs + (kb * 32 + li) * ST + 16 * ks + 8 * hh);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          s[kb][b] = mfma32(ak, qf[b][ks], s[kb][b]);
+          dp[kb][b] = mfma32(av, df[b][ks], dp[kb][b]);
+        }
+      }
+
+    if (partial || (kt + 1) * BN > P.Tk) {
+      const int aux = partial ? P.t.ent_aux[it] : -1;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int row = row_base + b * 32 + li;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const uint32_t bits = keymask32(P.m, aux, mg, partial, row, kt * BN + kb * 32);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = 16 * (r >> 3) + 8 * hh + (r & 7);
+            if (!((bits >> off) & 1u)) s[kb][b][r] = -INFINITY;
+          }
+        }
+      }
+    }
+
+    // dS^T = P^T (dP^T - D), kept in s[] as fp32.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][b][r], P.scale_log2, -lse2[b]));
+          s[kb][b][r] = pv * (dp[kb][b][r] - dlt[b]);
+        }
+
+    // dQ^T += K^T dS^T: A = K^T read transposed from the permuted K tile.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        bf16x8 sb[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) sb[b] = to_bf16x8(s[kb][b], 8 * t2);
+        // keys 16 t2 + 8 hh + 0..3 live in LDS rows 16 t2 + 4 hh + 0..3, keys +4..7 in rows +8
+        const int krow = kb * 32 + 16 * t2 + 4 * hh + tr_row(lane);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int kcol = db * 32 + tr_col(lane);
+          const bf16x8 a = ld_tr8(Ks + krow * ST + kcol, Ks + (krow + 8) * ST + kcol);
+#pragma unroll
+          for (int b = 0; b < 2; ++b) acc[db][b] = mfma32(a, sb[b], acc[db][b]);
+        }
+      }
+  }
+
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int row = row_base + b * 32 + li;
+    if (row >= P.Tq) continue;
+    bf16* dst = P.dq + ((int64_t)row * P.Hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        bf16x4 v4;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) v4[x] = (bf16)(acc[db][b][4 * rg + x] * P.scale);
+        *reinterpret_cast<bf16x4*>(dst + db * 32 + 8 * rg + 4 * hh) = v4;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK/dV kernel: one workgroup per (KV head, 128-key tile), four waves of 32
+// keys each.  K and V of the wave's keys stay in registers; for every query
+// head of the GQA group and every query tile (64 rows) in the key tile's
+// list, the Q / dO tiles and their LSE / delta rows are staged in LDS and
+//   S = Q K^T, dP = dO V^T           (queries x keys; lane = key)
+//   P = exp2(S scale log2e - LSE log2e), dS = P (dP - D)
+//   dV += P^T dO, dK += dS^T Q       (dO and Q read transposed from LDS)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
+  constexpr int BM = BM1, BN = BN1, ST = lds_stride<D>(), NKS = D / 16, NDB = D / 32;
+  constexpr int CPR = D / 8, CH = BM * CPR / 256;
+  __shared__ __attribute__((aligned(16))) bf16 Qs[BM * ST];
+  __shared__ __attribute__((aligned(16))) bf16 Ds[BM * ST];
+  __shared__ __attribute__((aligned(16))) float lse_s[BM];
+  __shared__ __attribute__((aligned(16))) float dlt_s[BM];
+  __shared__ uint32_t mask_s[BM * 4];
+
+  const int L = blockIdx.x;
+  const int kt = P.t.order[L / P.Hkv];
+  const int g = L % P.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, li = lane & 31;
+  const int key = kt * BN + w * 32 + li;
+  const bool kin = key < P.Tk;
+
+  // K, V of this lane's key as B operands: lane holds K[key][16ks + 8hh .. +8].
+  bf16x8 kf[NKS], vf[NKS];
+  {
+    const bf16* ks_ = P.k + (int64_t)key * P.k_tok + (int64_t)g * P.k_head + 8 * hh;
+    const bf16* vs_ = P.v + (int64_t)key * P.v_tok + (int64_t)g * P.v_head + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      kf[ks] = kin ? ld16(ks_ + 16 * ks) : bf16x8{};
+      vf[ks] = kin ? ld16(vs_ + 16 * ks) : bf16x8{};
+    }
+  }
+  f32x16 dka[NDB], dva[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dka[db] = f32x16{};
+    dva[db] = f32x16{};
+  }
+
+  for (int e = 0; e < P.R; ++e) {
+    const int h = g * P.R + e;
+    const int mg = h / P.grp_div;
+    const int32_t* ptr = P.t.ptr + (int64_t)mg * (P.t.nmajor + 1);
+    const int beg = ptr[kt], end = ptr[kt + 1];
+    for (int it = beg; it < end; ++it) {
+      const uint32_t ent = (uint32_t)P.t.ent[it];
+      const int qt = (int)(ent & 0x7fffffffu);
+      const bool partial = (ent & ENT_PARTIAL) != 0;
+      const int q0 = qt * BM;
+      u32x4 qr[CH], dr[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int id = tid + 256 * c, row = id / CPR, col = (id % CPR) * 8;
+        const int qrow = q0 + row;
+        if (qrow < P.Tq) {
+          qr[c] = gld16(P.q + (int64_t)qrow * P.q_tok + (int64_t)h * P.q_head + col);
+          dr[c] = gld16(P.d_o + ((int64_t)qrow * P.Hq + h) * D + col);
+        } else {
+          qr[c] = u32x4{};
+          dr[c] = u32x4{};
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int id = tid + 256 * c, row = id / CPR, col = (id % CPR) * 8;
+        st16(Qs + row * ST + col, qr[c]);
+        st16(Ds + row * ST + col, dr[c]);
+      }
+      if (tid < BM) {
+        const int qrow = q0 + tid;
+        const float l = qrow < P.Tq ? P.lse_in[(int64_t)h * P.Tq + qrow] : -INFINITY;
+        lse_s[tid] = (l == -INFINITY) ? INFINITY : l * LOG2E;
+        dlt_s[tid] = qrow < P.Tq ? P.delta[(int64_t)h * P.Tq + qrow] : 0.f;
+      }
+      if (partial) {
+        const int row = tid >> 2, word = tid & 3;
+        mask_s[tid] = keymask32(P.m, P.t.ent_aux[it], mg, true, q0 + row, kt * BN + 32 * word);
+      }
+      __syncthreads();
+
+      // S, dP for 2 query blocks of 32 rows x this wave's 32 keys.
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        s[b] = f32x16{};
+        dp[b] = f32x16{};
+      }
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const bf16x8 aq = ld16(Qs + (b * 32 + li) * ST + 16 * ks + 8 * hh);
+          const bf16x8 ad = ld16(Ds + (b * 32 + li) * ST + 16 * ks + 8 * hh);
+          s[b] = mfma32(aq, kf[ks], s[b]);
+          dp[b] = mfma32(ad, vf[ks], dp[b]);
+        }
+
+      // P and dS; register r of block b holds query row b*32 + 8(r/4) + 4hh + r%4.
+      f32x16 ds[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int rr = b * 32 + 8 * rg + 4 * hh;
+          const float4 l4 = *reinterpret_cast<const float4*>(lse_s + rr);
+          const float4 d4 = *reinterpret_cast<const float4*>(dlt_s + rr);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv_[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int r = 4 * rg + x;
+            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], P.scale_log2, -lv[x]));
+            if (partial && !((mask_s[(rr + x) * 4 + w] >> li) & 1u)) pv = 0.f;
+            s[b][r] = pv;
+            ds[b][r] = pv * (dp[b][r] - dv_[x]);
+          }
+        }
+
+      // dV += P^T dO and dK += dS^T Q over the 64 query rows (4 k-steps of 16).
+      // Contraction element e of lane half hh in k-step (b, t2) is query row
+      // b*32 + 16 t2 + 8(e/4) + 4hh + e%4 -- registers 8 t2 .. 8 t2 + 7.
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const bf16x8 pa = to_bf16x8(s[b], 8 * t2);
+          const bf16x8 sa = to_bf16x8(ds[b], 8 * t2);
+          const int qrow = b * 32 + 16 * t2 + 4 * hh + tr_row(lane);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const int col = db * 32 + tr_col(lane);
+            const bf16x8 bd = ld_tr8(Ds + qrow * ST + col, Ds + (qrow + 8) * ST + col);
+            const bf16x8 bq = ld_tr8(Qs + qrow * ST + col, Qs + (qrow + 8) * ST + col);
+            dva[db] = mfma32(pa, bd, dva[db]);
+            dka[db] = mfma32(sa, bq, dka[db]);
+          }
+        }
+    }
+  }
+
+  // dK, dV: lane holds column d = db*32 + li of key rows 8(r/4) + 4hh + r%4 of the wave's 32 keys.
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kk = kt * BN + w * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      if (kk < P.Tk) {
+        const int64_t off = ((int64_t)kk * P.Hkv + g) * D + db * 32 + li;
+        P.dk[off] = (bf16)(dka[db][r] * P.scale);
+        P.dv[off] = (bf16)dva[db][r];
+      }
+    }
+}
+
+hipError_t launch_bwd(const AttnParams& Pq, const AttnParams& Pkv, int D, int nq_items, int nkv_items,
+                      hipStream_t stream) {
+  const int64_t nrows = (int64_t)Pq.Tq * Pq.Hq;
+  if (nrows > 0) {
+    const int64_t threads = nrows * (D / 8);
+    const int nb = (int)((threads + 255) / 256);
+    if (D == 128) hipLaunchKernelGGL(delta_kernel<128>, dim3(nb), dim3(256), 0, stream, Pq);
+    else hipLaunchKernelGGL(delta_kernel<64>, dim3(nb), dim3(256), 0, stream, Pq);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (nkv_items > 0) {
+    if (D == 128) hipLaunchKernelGGL(dkdv_kernel<128>, dim3(nkv_items), dim3(256), 0, stream, Pkv);
+    else hipLaunchKernelGGL(dkdv_kernel<64>, dim3(nkv_items), dim3(256), 0, stream, Pkv);
+  }
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (nq_items > 0) {
+    if (D == 128) hipLaunchKernelGGL(dq_kernel<128>, dim3(nq_items), dim3(128), 0, stream, Pq);
+    else hipLaunchKernelGGL(dq_kernel<64>, dim3(nq_items), dim3(128), 0, stream, Pq);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mad

@@ -1,0 +1,209 @@
+// attn_fwd.hip -- forward attention kernel for gfx950.
+//
+// Computes, per query head h and query row i with allowed key set A_i,
+//   O_i = sum_j softmax_j(scale * q_i . k_j) v_j   and   LSE_i = ln sum_j exp(scale * q_i . k_j),
+// the standard softmax attention whose quadratic cost the LongCA-bench pages
+// start from (section 1), under a compiled mask.  A row with no allowed key
+// gets O = 0, LSE = -inf.
+//
+// Work decomposition: one workgroup per (query head, 128-row query tile), two
+// wave64s of 64 rows each.  The workgroup walks the query tile's list of
+// non-EMPTY 64-key tiles; K and V tiles are staged through LDS (the next
+// tile's global loads are in flight while the current one is computed).  Per
+// key tile each wave
+//   1. forms S^T = K Q^T (keys x queries) with bf16 MFMA; each lane then holds
+//      one query row, so the row max and row sum stay in the lane (plus one
+//      permlane32 swap with the other half-wave);
+//   2. masks PARTIAL tiles (and the ragged last key tile) with -inf;
+//   3. updates the online softmax in the exp2 domain (running max m, sum l,
+//      rescale factor alpha = exp2(m_old - m_new));
+//   4. accumulates O^T += V^T P^T with P^T taken straight from registers as
+//      the MFMA B operand and V^T read transposed from LDS.
+#include "kernel_common.hpp"
+
+namespace mad {
+
+template <int D>
+__global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
+  constexpr int BM = BM0, BN = BN0, ST = lds_stride<D>(), NKS = D / 16, NDB = D / 32;
+  constexpr int CPR = D / 8;            // 16-byte chunks per row
+  constexpr int CH = BN * CPR / 128;    // chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) bf16 Ks[BN * ST];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[BN * ST];
+
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int e = L % P.R, t_ = L / P.R;
+  const int g = t_ % P.Hkv, rank = t_ / P.Hkv;
+  const int h = g * P.R + e;
+  const int qt = P.t.order[rank];
+  const int mg = h / P.grp_div;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, li = lane & 31;
+  const int row_base = qt * BM + w * 64;
+
+  // Q as the B operand of S^T = K Q^T: lane holds Q[row][16ks + 8hh .. +8].
+  bf16x8 qf[2][NKS];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int row = row_base + b * 32 + li;
+    const bf16* src = P.q + (int64_t)row * P.q_tok + (int64_t)h * P.q_head + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (row < P.Tq) qf[b][ks] = ld16(src + 16 * ks);
+      else qf[b][ks] = bf16x8{};
+    }
+  }
+
+  f32x16 acc[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[db][b] = f32x16{};
+  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
+
+  const int32_t* ptr = P.t.ptr + (int64_t)mg * (P.t.nmajor + 1);
+  const int beg = ptr[qt], end = ptr[qt + 1];
+
+  u32x4 kr[CH], vr[CH];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int id = tid + 128 * c, row = id / CPR, col = (id % CPR) * 8;
+      const int key = kt * BN + row;
+      if (key < P.Tk) {
+        kr[c] = gld16(P.k + (int64_t)key * P.k_tok + (int64_t)g * P.k_head + col);
+        vr[c] = gld16(P.v + (int64_t)key * P.v_tok + (int64_t)g * P.v_head + col);
+      } else {
+        kr[c] = u32x4{};
+        vr[c] = u32x4{};
+      }
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int id = tid + 128 * c, row = id / CPR, col = (id % CPR) * 8;
+      st16(Ks + ((row & 32) | swap23(row & 31)) * ST + col, kr[c]);
+      st16(Vs + row * ST + col, vr[c]);
+    }
+  };
+
+  if (beg < end) gload(P.t.ent[beg] & 0x7fffffff);
+  for (int it = beg; it < end; ++it) {
+    const uint32_t ent = (uint32_t)P.t.ent[it];
+    const int kt = (int)(ent & 0x7fffffffu);
+    const bool partial = (ent & ENT_PARTIAL) != 0;
+    __syncthreads();
+    lstore();
+    __syncthreads();
+    if (it + 1 < end) gload(P.t.ent[it + 1] & 0x7fffffff);
+
+    // 1. S^T for 2 key blocks x 2 query blocks.
+    f32x16 s[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) s[kb][b] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = ld16(Ks + (kb * 32 + li) * ST + 16 * ks + 8 * hh);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) s[kb][b] = mfma32(a, qf[b][ks], s[kb][b]);
+      }
+
+    // 2. Mask.
+    if (partial || (kt + 1) * BN > P.Tk) {
+      const int aux = partial ? P.t.ent_aux[it] : -1;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int row = row_base + b * 32 + li;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const uint32_t bits = keymask32(P.m, aux, mg, partial, row, kt * BN + kb * 32);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = 16 * (r >> 3) + 8 * hh + (r & 7);
+            if (!((bits >> off) & 1u)) s[kb][b][r] = -INFINITY;
+          }
+        }
+      }
+    }
+
+    // 3. Online softmax (exp2 domain).
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][b][r]);
+      mx = pair_max(mx);
+      const float mnew = fmaxf(mrow[b], mx * P.scale_log2);
+      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+      const float alpha = __builtin_amdgcn_exp2f(mrow[b] - muse);
+      mrow[b] = mnew;
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][b][r], P.scale_log2, -muse));
+          s[kb][b][r] = pv;
+          ls += pv;
+        }
+      lrow[b] = lrow[b] * alpha + ls;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][b][r] *= alpha;
+    }
+
+    // 4. O^T += V^T P^T.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        bf16x8 pb[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) pb[b] = to_bf16x8(s[kb][b], 8 * t2);
+        const int vrow = kb * 32 + 16 * t2 + 8 * hh + tr_row(lane);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int vcol = db * 32 + tr_col(lane);
+          const bf16x8 a = ld_tr8(Vs + vrow * ST + vcol, Vs + (vrow + 4) * ST + vcol);
+#pragma unroll
+          for (int b = 0; b < 2; ++b) acc[db][b] = mfma32(a, pb[b], acc[db][b]);
+        }
+      }
+  }
+
+  // Epilogue: O = O^T / l, LSE = (m + log2 l) ln 2.
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const float lt = pair_sum(lrow[b]);
+    const int row = row_base + b * 32 + li;
+    if (row >= P.Tq) continue;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    bf16* dst = P.o + ((int64_t)row * P.Hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        bf16x4 v4;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) v4[x] = (bf16)(acc[db][b][4 * rg + x] * inv);
+        *reinterpret_cast<bf16x4*>(dst + db * 32 + 8 * rg + 4 * hh) = v4;
+      }
+    if (hh == 0) P.lse[(int64_t)h * P.Tq + row] = lt > 0.f ? (mrow[b] + __log2f(lt)) * LN2 : -INFINITY;
+  }
+}
+
+hipError_t launch_fwd(const AttnParams& P, int D, int n_items, hipStream_t stream) {
+  if (n_items <= 0) return hipSuccess;
+  if (D == 128) hipLaunchKernelGGL(fwd_kernel<128>, dim3(n_items), dim3(128), 0, stream, P);
+  else hipLaunchKernelGGL(fwd_kernel<64>, dim3(n_items), dim3(128), 0, stream, P);
+  return hipGetLastError();
+}
+
+}  // namespace mad

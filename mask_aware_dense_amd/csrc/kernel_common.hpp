@@ -1,0 +1,171 @@
+// kernel_common.hpp -- device helpers shared by the attention kernels (gfx950).
+//
+// Matrix products use the CDNA4 bf16 MFMA v_mfma_f32_32x32x16_bf16 with
+// fp32 accumulation.  Its lane layout (wave64, l = lane, h = l / 32):
+//   A (32 x 16): lane l holds A[l % 32][8h .. 8h+7]
+//   B (16 x 32): lane l holds B[8h .. 8h+7][l % 32]
+//   C (32 x 32): lane l, register r holds C[8(r/4) + 4h + (r%4)][l % 32]
+// The transposed LDS read ds_read_b64_tr_b16 lets 16-lane groups fetch an
+// operand whose contraction index runs along LDS rows: when lane 16G + i
+// points at row k0 + i/4, column n0 + 16(G%2) + 4(i%4), lane l receives the
+// four elements X[k0 + e][n0 + l % 32], e = 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.hpp"
+
+namespace mad {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+// LDS row stride (elements) of a [rows][D] bf16 tile: the padding keeps both
+// the 16-byte row reads of 16 consecutive rows and the 4-row transposed reads
+// on distinct banks of the 64-bank LDS (stride 76 dwords for D=128, 36 for D=64).
+template <int D>
+constexpr int lds_stride() { return D == 128 ? 152 : 72; }
+
+// Everything a kernel needs about one attention call.
+struct AttnParams {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  bf16* o;
+  float* lse;
+  const bf16* o_in;   // backward: forward output
+  const bf16* d_o;    // backward: upstream gradient (packed [Tq, Hq, D])
+  const float* lse_in;
+  float* delta;       // backward: rowsum(dO * O), [Hq, Tq]
+  bf16* dq;
+  bf16* dk;
+  bf16* dv;
+  int64_t q_tok, q_head, k_tok, k_head, v_tok, v_head;
+  int32_t Tq, Tk, Hq, Hkv;
+  int32_t R;        // Hq / Hkv
+  int32_t grp_div;  // Hq / n_groups (mask group of head h = h / grp_div)
+  float scale;      // softmax scale
+  float scale_log2; // scale * log2(e)
+  TilingDev t;
+  MaskDev m;
+};
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 ld16(const bf16* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st16(bf16* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ u32x4 gld16(const bf16* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Two transposed 4-element reads stacked into one 8-element MFMA operand.
+// row0 / row1 address the LDS rows of elements 0..3 and 4..7.
+__device__ __forceinline__ bf16x8 ld_tr8(const bf16* row0, const bf16* row1) {
+  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(row0));
+  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(row1));
+  u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  u32x4 r = {ua[0], ua[1], ub[0], ub[1]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Lane offsets of the transposed read inside a 16-lane group: row within
+// the 4-row group and column within the 32-column block.
+__device__ __forceinline__ int tr_row(int lane) { return (lane & 15) >> 2; }
+__device__ __forceinline__ int tr_col(int lane) { return 16 * ((lane >> 4) & 1) + 4 * (lane & 3); }
+
+// Eight fp32 values to an 8 x bf16 MFMA operand (round to nearest even).
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& s, int base) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)s[base + e];
+  return r;
+}
+
+// max / sum of x over lanes l and l ^ 32 (the two half-waves hold the same
+// query row in the transposed score layout).
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Swap bits 2 and 3 of a row index inside a 32-row block.  K (and V) tiles
+// are stored in LDS with row p holding key swap23(p): the score MFMA then
+// leaves keys 16(r/8) + 8h + (r%8) in register r of lane half h, so each
+// half-wave holds 8 consecutive keys per 8 registers -- the layout of the
+// next MFMA's contraction operand.
+__device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// Block index remap so that 8 consecutive logical work items (the query
+// heads of one GQA group at one tile) land on the same XCD: workgroups are
+// dispatched round-robin over the 8 XCDs, each with its own L2.
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  const int full = n - n % 64;
+  if (b >= full) return b;
+  const int loc = b & 63;
+  return (b - loc) + (loc & 7) * 8 + (loc >> 3);
+}
+
+__device__ __forceinline__ uint32_t range_bits(int a, int b) {
+  a = max(a, 0);
+  b = min(b, 32);
+  if (a >= b) return 0u;
+  const uint32_t hi = (b == 32) ? 0xffffffffu : ((1u << b) - 1u);
+  return hi & ~((1u << a) - 1u);
+}
+
+// Allowed keys of query row i among keys [key0, key0 + 32) of a visited tile,
+// as a bitmask (bit j <-> key key0 + j).  FULL tiles allow every in-range
+// key; PARTIAL tiles evaluate the mask source: the tile's slice list (SLICES)
+// or the block keep bitmap (BLOCKS).  Keys >= Tk are never allowed.
+__device__ __forceinline__ uint32_t keymask32(const MaskDev& m, int32_t aux, int32_t grp, bool partial, int i,
+                                              int key0) {
+  uint32_t bits;
+  if (!partial) {
+    bits = 0xffffffffu;
+  } else if (m.mode == MODE_SLICES) {
+    bits = 0u;
+    const int32_t* lst = m.tile_slices + aux;
+    const int n = lst[0];
+    for (int x = 0; x < n; ++x) {
+      const mad_slice s = m.slices[lst[1 + x]];
+      if (i < s.q0 || i >= s.q1) continue;
+      int lo = s.k0, hi = s.k1;
+      if (s.type == MAD_SLICE_CAUSAL) {
+        const int off = i - s.q0;
+        hi = min(hi, s.k0 + off + 1);
+        if (s.window > 0) lo = max(lo, s.k0 + off - s.window + 1);
+      }
+      bits |= range_bits(lo - key0, hi - key0);
+    }
+  } else {
+    bits = 0u;
+    const int kend = min(key0 + 32, m.Tk) - 1;
+    if (i < m.Tq && key0 <= kend) {
+      const int qb = m.row_qb[i];
+      const int ka = m.col_kb[key0], kz = m.col_kb[kend];
+      const uint64_t* row = m.keep + ((size_t)grp * m.n_qb + qb) * m.nw;
+      for (int kb = ka; kb <= kz; ++kb)
+        if ((row[kb >> 6] >> (kb & 63)) & 1ull) bits |= range_bits(m.k_edges[kb] - key0, m.k_edges[kb + 1] - key0);
+    }
+  }
+  const int nvalid = m.Tk - key0;
+  if (nvalid < 32) bits &= (nvalid <= 0) ? 0u : ((1u << nvalid) - 1u);
+  return bits;
+}
+
+}  // namespace mad

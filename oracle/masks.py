@@ -88,11 +88,12 @@ def _answer_segment(T, question, n_answers, pos):
     """Segment id: 0 for the question, 1..n for answers (equal split of the rest)."""
     rest = T - question
     base = rest // n_answers
-    seg = np.zeros_like(pos)
     a = pos - question
-    ans = np.where(a >= 0, np.minimum(a // max(base, 1), n_answers - 1) + 1, 0)
-    seg = np.where(pos < question, 0, ans)
-    return seg
+    if base > 0:
+        ans = np.minimum(a // base, n_answers - 1) + 1
+    else:  # fewer answer tokens than answers: the first n-1 answers are empty
+        ans = np.full_like(pos, n_answers)
+    return np.where(pos < question, 0, ans)
 
 
 def topk_keep(scores: np.ndarray, sparsity_pct: int) -> np.ndarray:
