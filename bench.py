@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Benchmark of the masked-attention hot path on one MI355X.
+
+Metric: effective attention TFLOP/s, counting only unmasked FLOPs, for the
+forward and for forward + backward, against the bf16 MFMA peak.  One step is
+one pass of the whole path over the workload: forward (O, LSE), then the
+backward's delta pre-pass, dK/dV kernel and dQ kernel.  Inputs are seeded
+synthetic bf16 N(0,1) tensors already resident in HBM; the mask plan is
+compiled and uploaded before timing (static masks are fixed before training,
+LongCA-bench section 2.1.1).  Timing follows the pages' protocol of warm-up
+steps before timed steps (appendix A.4: 5 warm-ups, 20 steps).
+
+Default workload: CAUSAL, one packed sequence of 32768 tokens, GQA 64 query
+heads : 8 KV heads, head dim 128.
+
+Prints one JSON line.  `--gpus N` with N > 1 is refused: this build runs on
+one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective attention TFLOP/s fwd and fwd+bwd (unmasked FLOPs) vs bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 MFMA peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seq", type=int, default=32768)
+    ap.add_argument("--hq", type=int, default=64)
+    ap.add_argument("--hkv", type=int, default=8)
+    ap.add_argument("--d", type=int, default=128)
+    ap.add_argument("--mask", default="CAUSAL")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-rows", type=int, default=96, help="query rows in the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fwd-only", action="store_true", help="time only the forward (profiling aid)")
+    return ap.parse_args()
+
+
+def cpu_baseline(args, q, k, v, do, spec, scale):
+    """Oracle (fp64 numpy, as it stands) on a bounded sample of the same workload."""
+    from oracle import attention as A
+    from oracle import masks as M
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info() if x.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    rng = np.random.default_rng([args.seed, 9])
+    rows = np.sort(rng.choice(args.seq, size=min(args.cpu_rows, args.seq), replace=False))
+    qf, kf, vf, dof = (A.to_f64(x) for x in (q, k, v, do))
+    t0 = time.perf_counter()
+    A.attn_fwd(qf, kf, vf, spec, scale, rows=rows)
+    A.attn_bwd(qf, kf, vf, dof, spec, scale, rows=rows)
+    dt = time.perf_counter() - t0
+    pairs = int(M.allowed(spec, rows, np.arange(args.seq)).sum()) * args.hq
+    flop = 14.0 * args.d * pairs
+    return {
+        "value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "seconds": dt,
+        "sample": f"{len(rows)} seeded query rows x {args.hq} heads of the same workload, fp64 forward + "
+                  f"backward (those rows' share of dQ, dK, dV); effective FLOPs 14*d*pairs",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "detail": "no collectives or sharding are built; see the design notes on sharding"}))
+        sys.exit(2)
+    import torch
+    import mask_aware_dense_amd as mad
+    from mad_inputs import grad_out, qkv
+    from oracle import masks as M
+
+    T, Hq, Hkv, d = args.seq, args.hq, args.hkv, args.d
+    scale = 1.0 / np.sqrt(d)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    q, k, v = qkv(args.seed, T, T, Hq, Hkv, d)
+    do = grad_out(args.seed, T, Hq, d)
+    qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
+
+    slices = mad.mask_slices(args.mask, T)
+    t0 = time.perf_counter()
+    plan = mad.mask_compile(slices, T, T)
+    compile_s = time.perf_counter() - t0
+    plan.upload()
+    st = plan.stats(0)
+    pairs_per_head = int(st["pairs"][0])
+    pairs = pairs_per_head * Hq
+    flop_fwd = 4.0 * d * pairs
+    flop_bwd = 10.0 * d * pairs
+
+    o = torch.empty_like(qd)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    ws = torch.empty(mad.bwd_workspace_bytes(plan, T, T, Hq, Hkv, d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    names = ["fwd", "delta", "dkdv", "dq"]
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        mad.attn_fwd(plan, qd, kd, vd, o, lse, scale, stream)
+        if evs is not None:
+            evs[1].record(stream)
+        if args.fwd_only:
+            return
+        for i, ph in enumerate((mad.BWD_DELTA, mad.BWD_DKDV, mad.BWD_DQ)):
+            mad.attn_bwd_phases(plan, qd, kd, vd, o, dod, lse, dq, dk, dv, ws, scale, ph, stream)
+            if evs is not None:
+                evs[2 + i].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    nk = 1 if args.fwd_only else 4
+    per = np.array([[evs[s][i].elapsed_time(evs[s][i + 1]) for i in range(nk)] for s in range(args.steps)])
+    kern_ms = {names[i]: float(np.mean(per[:, i])) for i in range(nk)}
+    kern_med = {names[i]: float(np.median(per[:, i])) for i in range(nk)}
+    ms_step = wall * 1e3 / args.steps
+    t_fwd = kern_ms["fwd"] * 1e-3
+    fwd_tflops = flop_fwd / t_fwd / 1e12
+    if args.fwd_only:
+        value = fwd_tflops
+    else:
+        value = (flop_fwd + flop_bwd) * args.steps / wall / 1e12
+
+    # Dominant kernel and its algorithmic work per launch: forward 4d FLOP per
+    # unmasked (query, key, head) pair; dK/dV kernel 8d (S, dP, dV, dK
+    # products); dQ kernel 2d (its dQ product -- its S and dP are recomputed,
+    # not algorithmic); the delta pre-pass is HBM-bound (reads O and dO).
+    alg = {"fwd": 4.0 * d * pairs, "dkdv": 8.0 * d * pairs, "dq": 2.0 * d * pairs}
+    dom = max(kern_ms, key=kern_ms.get)
+    if dom == "delta":
+        bytes_ = 2.0 * 2 * T * Hq * d + 4.0 * T * Hq
+        ach = bytes_ / (kern_ms[dom] * 1e-3) / 1e9
+        roof = {"kernel": "delta", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBS, "traffic": None}
+    else:
+        ach = alg[dom] / (kern_ms[dom] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / PEAK_BF16_TFLOPS, "traffic": None}
+
+    spec = M.MaskSpec(args.mask, T, T)
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.mask} attention {'fwd' if args.fwd_only else 'fwd+bwd'}, packed batch 1, "
+                               f"T={T}, GQA {Hq}:{Hkv}, head_dim {d}",
+                   "mask": args.mask, "seq_len": T, "heads_q": Hq, "heads_kv": Hkv, "head_dim": d,
+                   "parallelism": "single GPU"},
+        "fwd_tflops": fwd_tflops,
+        "fwd_frac_peak": fwd_tflops / PEAK_BF16_TFLOPS,
+        "fwdbwd_frac_peak": value / PEAK_BF16_TFLOPS,
+        "kernel_ms_mean": kern_ms,
+        "kernel_ms_median": kern_med,
+        "unmasked_pairs": pairs,
+        "mask_compile_s": compile_s,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args, q, k, v, do, spec, scale)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -215,6 +215,18 @@ mad_status mad_attn_bwd(const mad_plan* plan, const void* q, const void* k, cons
                         int32_t Tk, int32_t Hq, int32_t Hkv, int32_t d, const int64_t* strides,
                         float scale, hipStream_t stream);
 
+/* The same backward, restricted to a subset of its three launches:
+ * phases is a bit set of MAD_BWD_DELTA (the delta pre-pass), MAD_BWD_DKDV and
+ * MAD_BWD_DQ (which read the workspace's delta rows).  Calling the three
+ * phases in that order on one stream is equivalent to mad_attn_bwd; single
+ * phases let a caller time each kernel on its own. */
+enum { MAD_BWD_DELTA = 1, MAD_BWD_DKDV = 2, MAD_BWD_DQ = 4, MAD_BWD_ALL = 7 };
+mad_status mad_attn_bwd_phases(const mad_plan* plan, const void* q, const void* k, const void* v,
+                               const void* o, const void* d_o, const float* lse, void* dq, void* dk,
+                               void* dv, void* workspace, size_t workspace_bytes, int32_t Tq,
+                               int32_t Tk, int32_t Hq, int32_t Hkv, int32_t d, const int64_t* strides,
+                               float scale, uint32_t phases, hipStream_t stream);
+
 /* Message describing the last failure on the calling thread ("" if none). */
 const char* mad_last_error(void);
 

@@ -16,7 +16,8 @@ import numpy as np
 
 __all__ = [
     "MadError", "lib", "Plan", "mask_slices", "ring_step_slices", "block_topk",
-    "mask_compile", "sparse_plan", "attn_fwd", "attn_bwd", "bwd_workspace_bytes",
+    "mask_compile", "sparse_plan", "attn_fwd", "attn_bwd", "attn_bwd_phases", "bwd_workspace_bytes",
+    "BWD_DELTA", "BWD_DKDV", "BWD_DQ", "BWD_ALL",
     "PATTERNS", "SLICE_DTYPE",
 ]
 
@@ -29,6 +30,8 @@ PATTERNS = {
     "GLOBAL_SLIDING": 8, "CAUSAL_BLOCKWISE": 9, "BLOCK_CAUSAL_DOCUMENT": 10,
     "PREFIX_LM_DOCUMENT": 11,
 }
+
+BWD_DELTA, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 
 SLICE_DTYPE = np.dtype([("q0", "<i4"), ("q1", "<i4"), ("k0", "<i4"), ("k1", "<i4"),
                         ("type", "<i4"), ("window", "<i4")])
@@ -70,6 +73,8 @@ _SIGS = {
     "mad_bwd_workspace_bytes": (_I32, [_VP, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)]),
     "mad_attn_bwd": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
                             _I32, _I32, _I32, _I32, _I32, _VP, _F32, _VP]),
+    "mad_attn_bwd_phases": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
+                                   _I32, _I32, _I32, _I32, _I32, _VP, _F32, ctypes.c_uint32, _VP]),
     "mad_last_error": (ctypes.c_char_p, []),
     "mad_version": (ctypes.c_char_p, []),
 }
@@ -248,3 +253,15 @@ def attn_bwd(plan: Plan, q, k, v, o, d_o, lse, dq, dk, dv, workspace, scale: flo
     _check(lib().mad_attn_bwd(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
                               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes, Tq, Tk, Hq, Hkv, d,
                               st, float(scale), _stream(stream)))
+
+
+def attn_bwd_phases(plan: Plan, q, k, v, o, d_o, lse, dq, dk, dv, workspace, scale: float, phases: int,
+                    stream=None):
+    """One or more of the backward's launches (BWD_DELTA, BWD_DKDV, BWD_DQ bit set)."""
+    Tq, Hq, d = q.shape
+    Tk, Hkv, _ = k.shape
+    st = _qkv_strides(q, k, v)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().mad_attn_bwd_phases(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
+                                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes, Tq, Tk, Hq, Hkv, d,
+                                     st, float(scale), int(phases), _stream(stream)))

@@ -20,7 +20,7 @@ void clear_error() { g_err.clear(); }
 
 hipError_t launch_fwd(const AttnParams& P, int D, int n_items, hipStream_t stream);
 hipError_t launch_bwd(const AttnParams& Pq, const AttnParams& Pkv, int D, int nq_items, int nkv_items,
-                      hipStream_t stream);
+                      uint32_t phases, hipStream_t stream);
 
 namespace {
 
@@ -227,11 +227,13 @@ extern "C" mad_status mad_bwd_workspace_bytes(const mad_plan* p, int32_t Tq, int
   return MAD_OK;
 }
 
-extern "C" mad_status mad_attn_bwd(const mad_plan* p, const void* q, const void* k, const void* v, const void* o,
-                                   const void* d_o, const float* lse, void* dq, void* dk, void* dv, void* workspace,
-                                   size_t ws_bytes, int32_t Tq, int32_t Tk, int32_t Hq, int32_t Hkv, int32_t d,
-                                   const int64_t* strides, float scale, hipStream_t stream) {
+extern "C" mad_status mad_attn_bwd_phases(const mad_plan* p, const void* q, const void* k, const void* v,
+                                          const void* o, const void* d_o, const float* lse, void* dq, void* dk,
+                                          void* dv, void* workspace, size_t ws_bytes, int32_t Tq, int32_t Tk,
+                                          int32_t Hq, int32_t Hkv, int32_t d, const int64_t* strides, float scale,
+                                          uint32_t phases, hipStream_t stream) {
   clear_error();
+  if (phases == 0 || (phases & ~(uint32_t)MAD_BWD_ALL)) return fail(MAD_ERR_INVALID, "mad_attn_bwd: bad phase set");
   Strides st;
   mad_status s = check_common("mad_attn_bwd", p, q, k, v, Tq, Tk, Hq, Hkv, d, strides, st);
   if (s != MAD_OK) return s;
@@ -259,7 +261,15 @@ extern "C" mad_status mad_attn_bwd(const mad_plan* p, const void* q, const void*
   const int64_t nq = Tq > 0 ? (int64_t)p->tiling[0].nqt * Hq : 0;
   const int64_t nkv = Tk > 0 ? (int64_t)p->tiling[1].nkt * Hkv : 0;
   if (nq > INT32_MAX || nkv > INT32_MAX) return fail(MAD_ERR_UNSUPPORTED, "mad_attn_bwd: too many work items");
-  hipError_t e = launch_bwd(Pq, Pkv, d, (int)nq, (int)nkv, stream);
+  hipError_t e = launch_bwd(Pq, Pkv, d, (int)nq, (int)nkv, phases, stream);
   if (e != hipSuccess) return hip_fail("mad_attn_bwd: launch", e);
   return MAD_OK;
+}
+
+extern "C" mad_status mad_attn_bwd(const mad_plan* p, const void* q, const void* k, const void* v, const void* o,
+                                   const void* d_o, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                                   size_t ws_bytes, int32_t Tq, int32_t Tk, int32_t Hq, int32_t Hkv, int32_t d,
+                                   const int64_t* strides, float scale, hipStream_t stream) {
+  return mad_attn_bwd_phases(p, q, k, v, o, d_o, lse, dq, dk, dv, workspace, ws_bytes, Tq, Tk, Hq, Hkv, d, strides,
+                             scale, MAD_BWD_ALL, stream);
 }

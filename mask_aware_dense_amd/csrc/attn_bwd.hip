@@ -366,9 +366,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
 }
 
 hipError_t launch_bwd(const AttnParams& Pq, const AttnParams& Pkv, int D, int nq_items, int nkv_items,
-                      hipStream_t stream) {
+                      uint32_t phases, hipStream_t stream) {
   const int64_t nrows = (int64_t)Pq.Tq * Pq.Hq;
-  if (nrows > 0) {
+  if ((phases & MAD_BWD_DELTA) && nrows > 0) {
     const int64_t threads = nrows * (D / 8);
     const int nb = (int)((threads + 255) / 256);
     if (D == 128) hipLaunchKernelGGL(delta_kernel<128>, dim3(nb), dim3(256), 0, stream, Pq);
@@ -376,13 +376,13 @@ hipError_t launch_bwd(const AttnParams& Pq, const AttnParams& Pkv, int D, int nq
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (nkv_items > 0) {
+  if ((phases & MAD_BWD_DKDV) && nkv_items > 0) {
     if (D == 128) hipLaunchKernelGGL(dkdv_kernel<128>, dim3(nkv_items), dim3(256), 0, stream, Pkv);
     else hipLaunchKernelGGL(dkdv_kernel<64>, dim3(nkv_items), dim3(256), 0, stream, Pkv);
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (nq_items > 0) {
+  if ((phases & MAD_BWD_DQ) && nq_items > 0) {
     if (D == 128) hipLaunchKernelGGL(dq_kernel<128>, dim3(nq_items), dim3(128), 0, stream, Pq);
     else hipLaunchKernelGGL(dq_kernel<64>, dim3(nq_items), dim3(128), 0, stream, Pq);
   }
