@@ -46,6 +46,7 @@ STATIC_PATTERNS = (
 )
 SPARSE_PATTERNS = ("BLOCK_SPARSE", "VARIABLE_BLOCK_SPARSE")
 RING_PATTERNS = ("RING_STEP",)
+SLICE_PATTERNS = ("SLICES",)
 
 
 @dataclass
@@ -70,6 +71,8 @@ class MaskSpec:
     n_ranks: int = 1
     rank: int = 0
     source: int = 0
+    # SLICES: tuples (q0, q1, k0, k1, type 0=full 1=causal, window)
+    slices: tuple = ()
 
     @property
     def n_groups(self) -> int:
@@ -188,6 +191,18 @@ def allowed(spec: MaskSpec, rows, cols, group: int = 0) -> np.ndarray:
         gi = _ring_positions(spec, i, "q")
         gj = _ring_positions(spec, j, "k")
         return gi >= gj
+    if p == "SLICES":
+        # the unified mask format itself: union of (q_range, k_range, full |
+        # causal[, window]) slices, causal aligned at each slice's top-left
+        out = np.zeros((i.shape[0], j.shape[1]), dtype=bool)
+        for (q0, q1, k0, k1, typ, win) in spec.slices:
+            m = (i >= q0) & (i < q1) & (j >= k0) & (j < k1)
+            if typ == 1:
+                m = m & ((j - k0) <= (i - q0))
+                if win > 0:
+                    m = m & ((i - q0) - (j - k0) < win)
+            out |= m
+        return out
     raise ValueError(f"unknown mask pattern {p!r}")
 
 

@@ -1,0 +1,123 @@
+"""The C ABI library loads, exports every declared symbol, and rejects bad
+arguments with the documented status codes before touching the GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mask_aware_dense_amd as mad
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "mad.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mad_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert "mad_attn_fwd" in names and "mad_attn_bwd" in names and "mad_mask_compile" in names
+    L = mad.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert b"gfx950" in L.mad_version()
+
+
+def _status(e):
+    return e.value.status
+
+
+def test_mask_slice_errors():
+    with pytest.raises(mad.MadError) as e:
+        mad.mask_slices(99, 10)
+    assert _status(e) == 1
+    with pytest.raises(mad.MadError) as e:
+        mad.mask_slices("CAUSAL_DOCUMENT", 10, doc_lens=[3, 3])
+    assert _status(e) == 1 and "sum" in str(e.value)
+    with pytest.raises(mad.MadError):
+        mad.mask_slices("SLIDING_WINDOW", 10, window=0)
+    with pytest.raises(mad.MadError):
+        mad.ring_step_slices("headtail", 4, 7, 0, 1)  # odd chunk
+    with pytest.raises(mad.MadError):
+        mad.ring_step_slices("contiguous", 4, 8, 4, 1)  # rank out of range
+    with pytest.raises(mad.MadError):
+        mad.block_topk(np.zeros((1, 2, 3), np.float32), 101)
+    nan = np.zeros((1, 2, 3), np.float32)
+    nan[0, 1, 2] = np.nan
+    with pytest.raises(mad.MadError):
+        mad.block_topk(nan, 50)
+
+
+def test_compile_errors():
+    bad = np.array([(0, 11, 0, 5, 0, 0)], dtype=mad.SLICE_DTYPE)
+    with pytest.raises(mad.MadError) as e:
+        mad.mask_compile(bad, 10, 10)
+    assert _status(e) == 1 and "out of range" in str(e.value)
+    bad = np.array([(0, 5, 0, 5, 2, 0)], dtype=mad.SLICE_DTYPE)
+    with pytest.raises(mad.MadError):
+        mad.mask_compile(bad, 10, 10)
+    bad = np.array([(0, 5, 0, 5, 0, 3)], dtype=mad.SLICE_DTYPE)  # window on a FULL slice
+    with pytest.raises(mad.MadError):
+        mad.mask_compile(bad, 10, 10)
+    with pytest.raises(mad.MadError):
+        mad.sparse_plan(1, [0, 5, 5, 9], [0, 9], np.ones((1, 3, 1), np.uint64))
+    with pytest.raises(mad.MadError):
+        mad.sparse_plan(1, [1, 9], [0, 9], np.ones((1, 1, 1), np.uint64))
+
+
+class _Fake:
+    """Stand-in tensor: shape, strides and a (never dereferenced) address."""
+
+    def __init__(self, shape, addr=4096):
+        self.shape = shape
+        self._addr = addr
+        st = [1] * len(shape)
+        for i in range(len(shape) - 2, -1, -1):
+            st[i] = st[i + 1] * shape[i + 1]
+        self._st = st
+
+    def stride(self, i):
+        return self._st[i]
+
+    def data_ptr(self):
+        return self._addr
+
+    def numel(self):
+        return int(np.prod(self.shape))
+
+    def element_size(self):
+        return 1
+
+
+def test_attention_argument_errors_launch_nothing():
+    """Every check below fails before any HIP call (no GPU in this container)."""
+    T = 64
+    plan = mad.mask_compile(mad.mask_slices("CAUSAL", T), T, T)
+    q, k, v = _Fake((T, 4, 128)), _Fake((T, 2, 128)), _Fake((T, 2, 128))
+    o, lse = _Fake((T, 4, 128)), _Fake((4, T))
+    with pytest.raises(mad.MadError) as e:
+        mad.attn_fwd(plan, _Fake((T, 4, 96)), _Fake((T, 2, 96)), _Fake((T, 2, 96)), o, lse, 0.1, stream=0)
+    assert _status(e) == 2  # head dim
+    with pytest.raises(mad.MadError) as e:
+        mad.attn_fwd(plan, _Fake((T, 3, 128)), k, v, o, lse, 0.1, stream=0)
+    assert _status(e) == 1  # Hq % Hkv
+    with pytest.raises(mad.MadError) as e:
+        mad.attn_fwd(plan, _Fake((T + 1, 4, 128)), k, v, o, lse, 0.1, stream=0)
+    assert _status(e) == 1 and "compiled for" in str(e.value)
+    with pytest.raises(mad.MadError) as e:
+        mad.attn_fwd(plan, q, k, v, o, lse, 0.1, stream=0)
+    assert _status(e) == 1 and "not uploaded" in str(e.value)
+    with pytest.raises(mad.MadError) as e:
+        mad.attn_bwd(plan, q, k, v, o, q, lse, q, k, v, _Fake((16,)), 0.1, stream=0)
+    assert _status(e) == 1
+    with pytest.raises(mad.MadError) as e:
+        mad.attn_bwd_phases(plan, q, k, v, o, q, lse, q, k, v, _Fake((1 << 20,)), 0.1, 8, stream=0)
+    assert _status(e) == 1 and "phase" in str(e.value)
+    assert mad.bwd_workspace_bytes(plan, T, T, 4, 2, 128) >= 4 * T * 4
+    L = mad.lib()
+    assert L.mad_attn_fwd(None, None, None, None, None, None, 1, 1, 1, 1, 64, None, ctypes.c_float(1.0), None) == 1
+    assert b"plan is NULL" in L.mad_last_error()

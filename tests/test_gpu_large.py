@@ -1,0 +1,81 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times: sampled rows against the oracle, and backward invariants
+that hold at any size for dK and dV (the oracle's dK/dV at these sizes would
+need every row)."""
+import numpy as np
+import pytest
+
+import _gpu
+from mad_inputs import doc_lengths, grad_out, qkv
+from oracle import attention as A
+from oracle import masks as M
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_run(spec, Hq, Hkv, d, seed, sl=None):
+    import mask_aware_dense_amd as mad
+    if sl is None:
+        sl = mad.mask_slices(spec.pattern, spec.Tq, **_gpu.spec_kwargs(spec))
+    plan = mad.mask_compile(sl, spec.Tq, spec.Tk)
+    q, k, v = qkv(seed, spec.Tq, spec.Tk, Hq, Hkv, d)
+    do = grad_out(seed, spec.Tq, Hq, d)
+    scale = 1.0 / np.sqrt(d)
+    print(f"case {spec.pattern} T={spec.Tq} Hq={Hq} Hkv={Hkv} d={d}", flush=True)
+    got = _gpu.gpu_attention(plan, q, k, v, do, scale)
+    return q, k, v, do, scale, got
+
+
+def _check_sampled(spec, q, k, v, do, scale, got, n_rows=48, seed=0, heads=None):
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.choice(spec.Tq, size=min(n_rows, spec.Tq), replace=False))
+    Hq = q.shape[1]
+    heads = list(range(Hq)) if heads is None else heads
+    O, L = A.attn_fwd(q, k, v, spec, scale, rows=rows, heads=heads)
+    g = A.attn_bwd(q, k, v, do, spec, scale, rows=rows, heads=heads, want=("dq",))
+    _gpu.check_close("o", got["o"][rows][:, heads], O[:, heads], _gpu.TOL_FWD)
+    _gpu.check_lse(got["lse"][heads][:, rows], L[heads])
+    _gpu.check_close("dq", got["dq"][rows][:, heads], g["dq"][:, heads], _gpu.TOL_BWD)
+
+
+def _check_bwd_invariants(got, do, nonempty, Hkv):
+    """sum_j dK_j = 0 per KV head; sum_j dV_j = sum over rows with >= 1 key of dO (summed over the group)."""
+    dk, dv = got["dk"], got["dv"]
+    T, Hq, d = do.shape
+    dof = do.float().numpy().astype(np.float64) * nonempty[:, :, None]
+    ref_dv = dof.reshape(T, Hkv, Hq // Hkv, d).sum(axis=(0, 2))
+    for g in range(Hkv):
+        nk = np.linalg.norm(dk[:, g])
+        print(f"kv head {g}: |sum dK|/|dK| = {np.linalg.norm(dk[:, g].sum(axis=0)) / nk:.2e}, "
+              f"|sum dV - ref|/|dV| = {np.linalg.norm(dv[:, g].sum(axis=0) - ref_dv[g]) / np.linalg.norm(dv[:, g]):.2e}",
+              flush=True)
+        assert np.linalg.norm(dk[:, g].sum(axis=0)) <= 1e-2 * nk, ("dk sum", g)
+        assert np.linalg.norm(dv[:, g].sum(axis=0) - ref_dv[g]) <= 1e-2 * max(np.linalg.norm(dv[:, g]), 1.0), ("dv sum", g)
+
+
+def test_causal_32k_gqa_64_8():
+    """The benchmarked workload: CAUSAL, T=32768, GQA 64:8, d=128."""
+    spec = M.MaskSpec("CAUSAL", 32768, 32768)
+    q, k, v, do, scale, got = _full_run(spec, 64, 8, 128, seed=0)
+    _check_sampled(spec, q, k, v, do, scale, got, n_rows=32, heads=[0, 7, 8, 33, 63])
+    _check_bwd_invariants(got, do, np.ones((32768, 64), bool), 8)
+
+
+@pytest.mark.parametrize("pattern", ["SLIDING_WINDOW_CAUSAL_DOCUMENT", "SHARED_QUESTION", "BLOCK_CAUSAL_DOCUMENT"])
+def test_16k_workload_masks(pattern):
+    T = 16384
+    docs = tuple(int(x) for x in doc_lengths(11, T))
+    spec = M.MaskSpec(pattern, T, T, doc_lens=docs, window=4096, block=1024)
+    q, k, v, do, scale, got = _full_run(spec, 16, 2, 128, seed=3)
+    _check_sampled(spec, q, k, v, do, scale, got, n_rows=24)
+    _check_bwd_invariants(got, do, np.ones((T, 16), bool), 2)
+
+
+def test_ring_step_full_shape():
+    """A head-tail ring step at its real shape: 8K local queries x 8K remote keys, GQA 64:8."""
+    import mask_aware_dense_amd as mad
+    C = 8192
+    spec = M.MaskSpec("RING_STEP", C, C, layout="headtail", n_ranks=12, rank=0, source=0)
+    sl = mad.ring_step_slices("headtail", 12, C, 0, 0)
+    q, k, v, do, scale, got = _full_run(spec, 64, 8, 128, seed=4, sl=sl)
+    _check_sampled(spec, q, k, v, do, scale, got, n_rows=24, heads=[0, 9, 63])

@@ -55,3 +55,93 @@ def test_static_patterns_small(idx, d):
     T = 1000 + 37 * idx  # ragged: never a multiple of the 128 / 64 tile sizes
     spec = small_specs(T, seed=idx)[idx]
     _run_case(spec, _plan_for(spec), 8, 2, d, seed=100 + idx)
+
+
+def _sparse(T, b, G, pct, seed, variable):
+    import mask_aware_dense_amd as mad
+    if variable:
+        edges = np.concatenate([[0], np.cumsum(variable_block_sizes(seed, T))]).astype(np.int64)
+    else:
+        edges = M.uniform_edges(T, b)
+    n = len(edges) - 1
+    scores = block_scores(seed, G, n, n)
+    plan = mad.sparse_plan(G, edges, edges, mad.block_topk(scores, pct))
+    spec = M.MaskSpec("VARIABLE_BLOCK_SPARSE" if variable else "BLOCK_SPARSE", T, T,
+                      q_edges=edges, k_edges=edges, keep=M.topk_keep(scores, pct))
+    return plan, spec
+
+
+@pytest.mark.parametrize("b,variable", [(64, False), (128, False), (0, True)])
+@pytest.mark.parametrize("pct", [20, 50, 80])
+@pytest.mark.parametrize("heads", [(8, 8), (8, 2)], ids=["mha", "gqa"])
+def test_block_sparse(b, variable, pct, heads):
+    """Uniform 64/128 blocks and variable [32, 256] blocks; one keep set per KV head."""
+    Hq, Hkv = heads
+    T = 2048 if not variable else 1777
+    plan, spec = _sparse(T, b, Hkv, pct, seed=pct + b + Hkv, variable=variable)
+    _run_case(spec, plan, Hq, Hkv, 128, seed=7)
+
+
+def test_block_sparse_ragged_uniform():
+    plan, spec = _sparse(1000, 64, 2, 50, seed=3, variable=False)  # last block of 40
+    _run_case(spec, plan, 4, 2, 64, seed=8)
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "headtail"])
+@pytest.mark.parametrize("rs", [(0, 0), (0, 7), (11, 3), (11, 11), (5, 9)])
+def test_ring_step(layout, rs):
+    """One rank's share of a 12-rank ring step at reduced chunk size (1024 tokens)."""
+    r, s = rs
+    C = 1024
+    spec = M.MaskSpec("RING_STEP", C, C, layout=layout, n_ranks=12, rank=r, source=s)
+    _run_case(spec, _plan_for(spec), 8, 1, 128, seed=20 + r * 12 + s)
+
+
+@pytest.mark.parametrize("T", [1, 17, 65, 129])
+def test_tiny_and_ragged(T):
+    for pat in ("CAUSAL", "FULL"):
+        spec = M.MaskSpec(pat, T, T)
+        _run_case(spec, _plan_for(spec), 2, 1, 64, seed=T)
+
+
+def test_empty_key_range_gives_zero_and_neg_inf():
+    """Tk = 0: every row has no allowed key -> O = 0, LSE = -inf, dQ = 0."""
+    import mask_aware_dense_amd as mad
+    plan = mad.mask_compile(np.zeros(0, dtype=mad.SLICE_DTYPE), 300, 0)
+    q, _, _ = qkv(1, 300, 1, 4, 2, 128)
+    k = q[:0, :2]
+    got = _gpu.gpu_attention(plan, q, k, k, grad_out(1, 300, 4, 128), 0.1)
+    assert np.all(got["o"] == 0) and np.all(np.isneginf(got["lse"])) and np.all(got["dq"] == 0)
+
+
+def test_rectangular_slices():
+    """Tq != Tk with an arbitrary overlapping slice union."""
+    import mask_aware_dense_amd as mad
+    sl = [(0, 300, 0, 500, 1, 0), (100, 700, 200, 450, 0, 0), (650, 777, 600, 901, 1, 37)]
+    spec = M.MaskSpec("SLICES", 777, 901, slices=tuple(sl))
+    plan = mad.mask_compile(np.array(sl, dtype=mad.SLICE_DTYPE), 777, 901)
+    _run_case(spec, plan, 4, 4, 128, seed=5)
+
+
+def test_strided_inputs_and_determinism():
+    """q, k, v as views of one fused [T, Hq + 2 Hkv, d] tensor; forward repeats bit for bit."""
+    import torch
+    import mask_aware_dense_amd as mad
+    T, Hq, Hkv, d = 700, 4, 2, 128
+    q, k, v = qkv(2, T, T, Hq, Hkv, d)
+    dev = torch.device("cuda", 0)
+    fused = torch.cat([q, k, v], dim=1).to(dev)
+    qv, kv, vv = fused[:, :Hq], fused[:, Hq:Hq + Hkv], fused[:, Hq + Hkv:]
+    spec = M.MaskSpec("CAUSAL", T, T)
+    plan = _plan_for(spec).upload()
+    outs = []
+    for _ in range(2):
+        o = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+        mad.attn_fwd(plan, qv, kv, vv, o, lse, 1 / np.sqrt(d))
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), lse.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    O, L = A.attn_fwd(q, k, v, spec, 1 / np.sqrt(d))
+    _gpu.check_close("o", outs[0][0].float().numpy(), O, _gpu.TOL_FWD)
+    _gpu.check_lse(outs[0][1].numpy(), L)

@@ -240,3 +240,25 @@ def test_ring_merge_equals_dense_causal(layout):
         Om, Lm = MG.merge(outs, lses)
         assert np.max(np.abs(Om - Oall[gq])) < 1e-13
         assert np.max(np.abs(Lm - Lall[:, gq])) < 1e-13
+
+
+def test_slice_union_matches_closed_forms():
+    """Hand-written slice lists (the unified format) rasterise to the closed-form masks."""
+    T = 50
+    P = T // 4
+    cases = [
+        ("CAUSAL", [(0, T, 0, T, 1, 0)], {}),
+        ("SLIDING_WINDOW", [(0, T, 0, T, 1, 7)], dict(window=7)),
+        ("PREFIX_LM", [(0, T, 0, P, 0, 0), (P, T, P, T, 1, 0)], {}),
+        ("GLOBAL_SLIDING", [(0, T, 0, T, 1, 9), (9, T, 0, 4, 1, 0)], dict(global_len=4, window=9)),
+        ("FULL_DOCUMENT", [(0, 20, 0, 20, 0, 0), (20, 50, 20, 50, 0, 0)], dict(doc_lens=(20, 30))),
+    ]
+    for pat, sl, kw in cases:
+        a = M.dense(M.MaskSpec("SLICES", T, T, slices=tuple(sl)))
+        b = M.dense(M.MaskSpec(pat, T, T, **kw))
+        assert np.array_equal(a, b), pat
+    # overlapping slices: the union counts each pair once
+    a = M.dense(M.MaskSpec("SLICES", T, T, slices=((0, T, 0, T, 1, 0), (0, T, 0, T, 1, 0), (5, 9, 0, 40, 0, 0))))
+    ref = np.tri(T, T, dtype=bool)
+    ref[5:9, 0:40] = True
+    assert np.array_equal(a, ref)
