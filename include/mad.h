@@ -199,15 +199,17 @@ mad_status mad_attn_fwd(const mad_plan* plan, const void* q, const void* k, cons
                         void* o, float* lse, int32_t Tq, int32_t Tk, int32_t Hq, int32_t Hkv,
                         int32_t d, const int64_t* strides, float scale, hipStream_t stream);
 
-/* Bytes of device workspace mad_attn_bwd needs (the delta rows, fp32 [Hq, Tq]). */
+/* Bytes of device workspace mad_attn_bwd needs: two fp32 [Hq][Tq rounded up
+ * to 128] arrays, the delta rows D = rowsum(dO * O) and LSE * log2(e) (+inf
+ * for rows with no allowed key and for padding rows). */
 mad_status mad_bwd_workspace_bytes(const mad_plan* plan, int32_t Tq, int32_t Tk, int32_t Hq,
                                    int32_t Hkv, int32_t d, size_t* bytes);
 
 /* Backward of the forward above for upstream gradient d_o, given o and lse
  * (normally the forward's; for a ring step the merged global ones, so the
  * step's share of the global gradient is produced).  Runs the delta pre-pass
- * D = rowsum(d_o * o) into the workspace, then the dK/dV kernel and the dQ
- * kernel.  dq, dk, dv are overwritten.  workspace must be 256-byte aligned
+ * D = rowsum(d_o * o) (and LSE * log2 e) into the workspace, then the dK/dV
+ * kernel and the dQ kernel.  dq, dk, dv are overwritten.  workspace must be 256-byte aligned
  * and at least mad_bwd_workspace_bytes long; q/k/v/o/d_o are not modified. */
 mad_status mad_attn_bwd(const mad_plan* plan, const void* q, const void* k, const void* v,
                         const void* o, const void* d_o, const float* lse, void* dq, void* dk,

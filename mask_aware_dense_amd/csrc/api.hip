@@ -223,7 +223,9 @@ extern "C" mad_status mad_bwd_workspace_bytes(const mad_plan* p, int32_t Tq, int
   if (!p) return fail(MAD_ERR_INVALID, "mad_bwd_workspace_bytes: plan is NULL");
   if (Tq < 0 || Tk < 0 || Hq <= 0 || Hkv <= 0) return fail(MAD_ERR_INVALID, "mad_bwd_workspace_bytes: bad sizes");
   if (d != 64 && d != 128) return fail(MAD_ERR_UNSUPPORTED, "mad_bwd_workspace_bytes: head dim must be 64 or 128");
-  *bytes = (((size_t)Hq * (size_t)Tq * 4) + 255) & ~(size_t)255;
+  // delta and lse2 rows, each [Hq][Tq rounded up to 128] fp32
+  const size_t tq_pad = ((size_t)Tq + 127) / 128 * 128;
+  *bytes = 2 * (size_t)Hq * tq_pad * 4;
   return MAD_OK;
 }
 
@@ -252,7 +254,9 @@ extern "C" mad_status mad_attn_bwd_phases(const mad_plan* p, const void* q, cons
   Pq.o_in = (const bf16*)o;
   Pq.d_o = (const bf16*)d_o;
   Pq.lse_in = lse;
+  Pq.Tq_pad = (int32_t)(((int64_t)Tq + 127) / 128 * 128);
   Pq.delta = (float*)workspace;
+  Pq.lse2 = (float*)workspace + (size_t)Hq * Pq.Tq_pad;
   Pq.dq = (bf16*)dq;
   Pq.dk = (bf16*)dk;
   Pq.dv = (bf16*)dv;

@@ -13,22 +13,28 @@
 // tile and walks the query tiles of its per-key-tile list for every query
 // head of its GQA group, and a dQ kernel that owns a query tile and walks its
 // key-tile list (the forward's tiling).  Both recompute P from LSE.
+//
+// Workspace (fp32, rows padded to a multiple of 128 per head):
+//   delta[h][i] = D_i and lse2[h][i] = LSE_i log2(e), with lse2 = +inf for rows
+//   that have no allowed key or lie past Tq -- so their P is exactly 0.
 #include "kernel_common.hpp"
 
 namespace mad {
 
 // ---------------------------------------------------------------------------
-// Delta pre-pass: D[h][i] = sum_c dO[i][h][c] * O[i][h][c] (fp32).
-// One group of D/8 lanes per (row, head); inputs packed [Tq, Hq, D].
+// Delta pre-pass.  One group of D/8 lanes per (row, head); O and dO packed
+// [Tq, Hq, D].
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void delta_kernel(const AttnParams P) {
   constexpr int LPR = D / 8;  // lanes per row
-  const int64_t nrows = (int64_t)P.Tq * P.Hq;
+  const int64_t nrows = (int64_t)P.Tq_pad * P.Hq;
   const int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;
   const int sub = threadIdx.x % LPR;
+  const int64_t i = r / P.Hq, h = r % P.Hq;
+  const bool in = r < nrows && i < P.Tq;
   float acc = 0.f;
-  if (r < nrows) {
+  if (in) {
     const bf16x8 a = ld16(P.o_in + r * D + 8 * sub);
     const bf16x8 b = ld16(P.d_o + r * D + 8 * sub);
 #pragma unroll
@@ -37,24 +43,29 @@ __global__ __launch_bounds__(256) void delta_kernel(const AttnParams P) {
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
   if (r < nrows && sub == 0) {
-    const int64_t i = r / P.Hq, h = r % P.Hq;
-    P.delta[h * P.Tq + i] = acc;
+    float l2 = INFINITY;
+    if (in) {
+      const float l = P.lse_in[h * P.Tq + i];
+      l2 = (l == -INFINITY) ? INFINITY : l * LOG2E;
+    }
+    P.delta[h * P.Tq_pad + i] = acc;
+    P.lse2[h * P.Tq_pad + i] = l2;
   }
 }
 
 // ---------------------------------------------------------------------------
 // dQ kernel: one workgroup per (query head, 128-row query tile), two waves of
-// 64 rows, walking the forward tiling's key-tile list.  Per key tile:
+// 64 rows, walking the forward tiling's key-tile list.  K and V tiles come in
+// by direct loads into a double buffer (both stored with the swap23 row order).
+// Per key block of 32 keys:
 //   S^T = K Q^T, dP^T = V dO^T       (keys x queries; lane = query row)
-//   P^T = exp2(S^T scale log2e - LSE log2e), dS^T = P^T (dP^T - D)
+//   P^T = exp2(S^T scale log2e - lse2), dS^T = P^T (dP^T - D)
 //   dQ^T += K^T dS^T                 (K^T read transposed from LDS)
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
-  constexpr int BM = BM0, BN = BN0, ST = lds_stride<D>(), NKS = D / 16, NDB = D / 32;
-  constexpr int CPR = D / 8, CH = BN * CPR / 128;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[BN * ST];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[BN * ST];
+  constexpr int BM = BM0, BN = BN0, NKS = D / 16, NDB = D / 32, TILE = tile_elems<D>(), RS = tile_rs<D>();
+  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // K0 V0 K1 V1
 
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int e = L % P.R, t_ = L / P.R;
@@ -65,23 +76,31 @@ __global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, li = lane & 31;
   const int row_base = qt * BM + w * 64;
 
+  const int32_t* ptr = P.t.ptr + (int64_t)mg * (P.t.nmajor + 1);
+  const int beg = ptr[qt], end = ptr[qt + 1];
+  const bf16* kg = P.k + (int64_t)g * P.k_head;
+  const bf16* vg = P.v + (int64_t)g * P.v_head;
+  auto issue = [&](int kt, int buf) {
+    tile_load_async<D, 2, true>(smem + (2 * buf) * TILE, kg, P.k_tok, kt * BN, P.Tk, w, lane);
+    tile_load_async<D, 2, true>(smem + (2 * buf + 1) * TILE, vg, P.v_tok, kt * BN, P.Tk, w, lane);
+  };
+  if (beg < end) issue(P.t.ent[beg] & 0x7fffffff, 0);
+
   bf16x8 qf[2][NKS], df[2][NKS];
   float lse2[2], dlt[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int row = row_base + b * 32 + li;
-    const bool in = row < P.Tq;
-    const bf16* qs = P.q + (int64_t)row * P.q_tok + (int64_t)h * P.q_head + 8 * hh;
-    const bf16* ds = P.d_o + ((int64_t)row * P.Hq + h) * D + 8 * hh;
+    const int rc = min(row, P.Tq - 1);
+    const bf16* qs = P.q + (int64_t)rc * P.q_tok + (int64_t)h * P.q_head + 8 * hh;
+    const bf16* ds = P.d_o + ((int64_t)rc * P.Hq + h) * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      qf[b][ks] = in ? ld16(qs + 16 * ks) : bf16x8{};
-      df[b][ks] = in ? ld16(ds + 16 * ks) : bf16x8{};
+      qf[b][ks] = ld16(qs + 16 * ks);
+      df[b][ks] = ld16(ds + 16 * ks);
     }
-    const float l = in ? P.lse_in[(int64_t)h * P.Tq + row] : -INFINITY;
-    // rows with no allowed key (LSE = -inf) and rows past Tq get P = 0
-    lse2[b] = (l == -INFINITY) ? INFINITY : l * LOG2E;
-    dlt[b] = in ? P.delta[(int64_t)h * P.Tq + row] : 0.f;
+    lse2[b] = P.lse2[(int64_t)h * P.Tq_pad + row];
+    dlt[b] = P.delta[(int64_t)h * P.Tq_pad + row];
   }
 
   f32x16 acc[NDB][2];
@@ -90,103 +109,73 @@ __global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[db][b] = f32x16{};
 
-  const int32_t* ptr = P.t.ptr + (int64_t)mg * (P.t.nmajor + 1);
-  const int beg = ptr[qt], end = ptr[qt + 1];
-
   for (int it = beg; it < end; ++it) {
+    const int buf = (it - beg) & 1;
     const uint32_t ent = (uint32_t)P.t.ent[it];
     const int kt = (int)(ent & 0x7fffffffu);
     const bool partial = (ent & ENT_PARTIAL) != 0;
-    u32x4 kr[CH], vr[CH];
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int id = tid + 128 * c, row = id / CPR, col = (id % CPR) * 8;
-      const int key = kt * BN + row;
-      if (key < P.Tk) {
-        kr[c] = gld16(P.k + (int64_t)key * P.k_tok + (int64_t)g * P.k_head + col);
-        vr[c] = gld16(P.v + (int64_t)key * P.v_tok + (int64_t)g * P.v_head + col);
-      } else {
-        kr[c] = u32x4{};
-        vr[c] = u32x4{};
-      }
-    }
+    const bool masked = partial || (kt + 1) * BN > P.Tk;
+    const int aux = partial ? P.t.ent_aux[it] : -1;
+    wait_vmem();
     __syncthreads();
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int id = tid + 128 * c, row = id / CPR, col = (id % CPR) * 8;
-      const int prow = (row & 32) | swap23(row & 31);
-      st16(Ks + prow * ST + col, kr[c]);
-      st16(Vs + prow * ST + col, vr[c]);
-    }
-    __syncthreads();
+    if (it + 1 < end) issue(P.t.ent[it + 1] & 0x7fffffff, buf ^ 1);
+    const bf16* Ks = smem + (2 * buf) * TILE;
+    const bf16* Vs = smem + (2 * buf + 1) * TILE;
 
-    f32x16 s[2][2], dp[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s[2], dp[2];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        s[kb][b] = f32x16{};
-        dp[kb][b] = f32x16{};
+        s[b] = f32x16{};
+        dp[b] = f32x16{};
       }
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 ak = ld16(Ks + (kb * 32 + li) * ST + 16 * ks + 8 * hh);
-        const bf16x8 av = ld16(Vs + (kb * 32 + li) * ST + 16 * ks + 8 * hh);
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int off = (kb * 32 + li) * RS + (16 * ks + 8 * hh);
+        const bf16x8 ak = ld16(Ks + off);
+        const bf16x8 av = ld16(Vs + off);
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-          s[kb][b] = mfma32(ak, qf[b][ks], s[kb][b]);
-          dp[kb][b] = mfma32(av, df[b][ks], dp[kb][b]);
+          s[b] = mfma32(ak, qf[b][ks], s[b]);
+          dp[b] = mfma32(av, df[b][ks], dp[b]);
         }
       }
-
-    if (partial || (kt + 1) * BN > P.Tk) {
-      const int aux = partial ? P.t.ent_aux[it] : -1;
+      if (masked) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int row = row_base + b * 32 + li;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const uint32_t bits = keymask32(P.m, aux, mg, partial, row, kt * BN + kb * 32);
+        for (int b = 0; b < 2; ++b) {
+          const uint32_t bits = keymask32(P.m, aux, mg, partial, row_base + b * 32 + li, kt * BN + kb * 32);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int off = 16 * (r >> 3) + 8 * hh + (r & 7);
-            if (!((bits >> off) & 1u)) s[kb][b][r] = -INFINITY;
+            if (!((bits >> off) & 1u)) s[b][r] = -INFINITY;
           }
         }
       }
-    }
-
-    // dS^T = P^T (dP^T - D), kept in s[] as fp32.
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      // dS^T = P^T (dP^T - D), in s[].
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][b][r], P.scale_log2, -lse2[b]));
-          s[kb][b][r] = pv * (dp[kb][b][r] - dlt[b]);
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], P.scale_log2, -lse2[b]));
+          s[b][r] = pv * (dp[b][r] - dlt[b]);
         }
-
-    // dQ^T += K^T dS^T: A = K^T read transposed from the permuted K tile.
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      // dQ^T += K^T dS^T: keys 16 t2 + 8 hh + 0..3 live in LDS rows 16 t2 + 4 hh + 0..3, keys +4..7 in rows +8.
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         bf16x8 sb[2];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) sb[b] = to_bf16x8(s[kb][b], 8 * t2);
-        // keys 16 t2 + 8 hh + 0..3 live in LDS rows 16 t2 + 4 hh + 0..3, keys +4..7 in rows +8
+        for (int b = 0; b < 2; ++b) sb[b] = to_bf16x8(s[b], 8 * t2);
         const int krow = kb * 32 + 16 * t2 + 4 * hh + tr_row(lane);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const int kcol = db * 32 + tr_col(lane);
-          const bf16x8 a = ld_tr8(Ks + krow * ST + kcol, Ks + (krow + 8) * ST + kcol);
+          const bf16x8 a = ld_tr8(Ks + (krow) * RS + (kcol), Ks + (krow + 8) * RS + (kcol));
 #pragma unroll
           for (int b = 0; b < 2; ++b) acc[db][b] = mfma32(a, sb[b], acc[db][b]);
         }
       }
+    }
   }
 
 #pragma unroll
@@ -210,19 +199,17 @@ __global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
 // dK/dV kernel: one workgroup per (KV head, 128-key tile), four waves of 32
 // keys each.  K and V of the wave's keys stay in registers; for every query
 // head of the GQA group and every query tile (64 rows) in the key tile's
-// list, the Q / dO tiles and their LSE / delta rows are staged in LDS and
+// list, the Q / dO tiles and their lse2 / delta rows arrive by direct loads
+// into a double buffer, and
 //   S = Q K^T, dP = dO V^T           (queries x keys; lane = key)
-//   P = exp2(S scale log2e - LSE log2e), dS = P (dP - D)
+//   P = exp2(S scale log2e - lse2), dS = P (dP - D)
 //   dV += P^T dO, dK += dS^T Q       (dO and Q read transposed from LDS)
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
-  constexpr int BM = BM1, BN = BN1, ST = lds_stride<D>(), NKS = D / 16, NDB = D / 32;
-  constexpr int CPR = D / 8, CH = BM * CPR / 256;
-  __shared__ __attribute__((aligned(16))) bf16 Qs[BM * ST];
-  __shared__ __attribute__((aligned(16))) bf16 Ds[BM * ST];
-  __shared__ __attribute__((aligned(16))) float lse_s[BM];
-  __shared__ __attribute__((aligned(16))) float dlt_s[BM];
+  constexpr int BM = BM1, BN = BN1, NKS = D / 16, NDB = D / 32, TILE = tile_elems<D>(), RS = tile_rs<D>();
+  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];   // Q0 dO0 Q1 dO1
+  __shared__ __attribute__((aligned(256))) float rowv[2][2 * BM];  // per buffer: lse2[64], delta[64]
   __shared__ uint32_t mask_s[BM * 4];
 
   const int L = blockIdx.x;
@@ -230,17 +217,17 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
   const int g = L % P.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, li = lane & 31;
   const int key = kt * BN + w * 32 + li;
-  const bool kin = key < P.Tk;
+  const int kc = min(key, P.Tk - 1);
 
   // K, V of this lane's key as B operands: lane holds K[key][16ks + 8hh .. +8].
   bf16x8 kf[NKS], vf[NKS];
   {
-    const bf16* ks_ = P.k + (int64_t)key * P.k_tok + (int64_t)g * P.k_head + 8 * hh;
-    const bf16* vs_ = P.v + (int64_t)key * P.v_tok + (int64_t)g * P.v_head + 8 * hh;
+    const bf16* ks_ = P.k + (int64_t)kc * P.k_tok + (int64_t)g * P.k_head + 8 * hh;
+    const bf16* vs_ = P.v + (int64_t)kc * P.v_tok + (int64_t)g * P.v_head + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      kf[ks] = kin ? ld16(ks_ + 16 * ks) : bf16x8{};
-      vf[ks] = kin ? ld16(vs_ + 16 * ks) : bf16x8{};
+      kf[ks] = ld16(ks_ + 16 * ks);
+      vf[ks] = ld16(vs_ + 16 * ks);
     }
   }
   f32x16 dka[NDB], dva[NDB];
@@ -250,105 +237,119 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
     dva[db] = f32x16{};
   }
 
-  for (int e = 0; e < P.R; ++e) {
-    const int h = g * P.R + e;
-    const int mg = h / P.grp_div;
-    const int32_t* ptr = P.t.ptr + (int64_t)mg * (P.t.nmajor + 1);
-    const int beg = ptr[kt], end = ptr[kt + 1];
-    for (int it = beg; it < end; ++it) {
-      const uint32_t ent = (uint32_t)P.t.ent[it];
-      const int qt = (int)(ent & 0x7fffffffu);
-      const bool partial = (ent & ENT_PARTIAL) != 0;
-      const int q0 = qt * BM;
-      u32x4 qr[CH], dr[CH];
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int id = tid + 256 * c, row = id / CPR, col = (id % CPR) * 8;
-        const int qrow = q0 + row;
-        if (qrow < P.Tq) {
-          qr[c] = gld16(P.q + (int64_t)qrow * P.q_tok + (int64_t)h * P.q_head + col);
-          dr[c] = gld16(P.d_o + ((int64_t)qrow * P.Hq + h) * D + col);
-        } else {
-          qr[c] = u32x4{};
-          dr[c] = u32x4{};
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int id = tid + 256 * c, row = id / CPR, col = (id % CPR) * 8;
-        st16(Qs + row * ST + col, qr[c]);
-        st16(Ds + row * ST + col, dr[c]);
-      }
-      if (tid < BM) {
-        const int qrow = q0 + tid;
-        const float l = qrow < P.Tq ? P.lse_in[(int64_t)h * P.Tq + qrow] : -INFINITY;
-        lse_s[tid] = (l == -INFINITY) ? INFINITY : l * LOG2E;
-        dlt_s[tid] = qrow < P.Tq ? P.delta[(int64_t)h * P.Tq + qrow] : 0.f;
-      }
-      if (partial) {
-        const int row = tid >> 2, word = tid & 3;
-        mask_s[tid] = keymask32(P.m, P.t.ent_aux[it], mg, true, q0 + row, kt * BN + 32 * word);
-      }
-      __syncthreads();
+  // Flattened walk over (query head of the group, query tile of that head's
+  // list), kept as two cursors: the item being computed and the next one,
+  // whose tiles are prefetched.
+  struct Cursor {
+    int e, it, end;
+  };
+  auto head_list = [&](int e, Cursor& c) {
+    const int32_t* ptr = P.t.ptr + (int64_t)((g * P.R + e) / P.grp_div) * (P.t.nmajor + 1);
+    c.e = e;
+    c.it = ptr[kt];
+    c.end = ptr[kt + 1];
+  };
+  auto settle = [&](Cursor& c) {  // move past exhausted heads
+    while (c.it >= c.end && c.e + 1 < P.R) head_list(c.e + 1, c);
+  };
+  auto issue = [&](const Cursor& c, int buf) {
+    const int hx = g * P.R + c.e;
+    const int q0 = (P.t.ent[c.it] & 0x7fffffff) * BM;
+    tile_load_async<D, 4, false>(smem + (2 * buf) * TILE, P.q + (int64_t)hx * P.q_head, P.q_tok, q0, P.Tq, w, lane);
+    tile_load_async<D, 4, false>(smem + (2 * buf + 1) * TILE, P.d_o + (int64_t)hx * D, (int64_t)P.Hq * D, q0, P.Tq,
+                                 w, lane);
+    if (w == 0 && lane < 32) {
+      const float* src = (lane < 16 ? P.lse2 : P.delta) + (int64_t)hx * P.Tq_pad + q0 + 4 * (lane & 15);
+      g2lds16(src, &rowv[buf][0]);
+    }
+  };
+  Cursor cur;
+  head_list(0, cur);
+  settle(cur);
+  if (cur.it < cur.end) issue(cur, 0);
 
-      // S, dP for 2 query blocks of 32 rows x this wave's 32 keys.
-      f32x16 s[2], dp[2];
+  for (int n = 0; cur.it < cur.end; ++n) {
+    const int buf = n & 1;
+    const int h = g * P.R + cur.e;
+    const int it = cur.it;
+    const int mg = h / P.grp_div;
+    const uint32_t ent = (uint32_t)P.t.ent[it];
+    const int qt = (int)(ent & 0x7fffffffu);
+    const bool partial = (ent & ENT_PARTIAL) != 0;
+    const int q0 = qt * BM;
+    Cursor nxt = cur;
+    ++nxt.it;
+    settle(nxt);
+    wait_vmem();
+    __syncthreads();
+    if (nxt.it < nxt.end) issue(nxt, buf ^ 1);
+    if (partial) {
+      mask_s[tid] = keymask32(P.m, P.t.ent_aux[it], mg, true, q0 + (tid >> 2), kt * BN + 32 * (tid & 3));
+      __syncthreads();
+    }
+    const bf16* Qs = smem + (2 * buf) * TILE;
+    const bf16* Ds = smem + (2 * buf + 1) * TILE;
+    const float* lse_s = &rowv[buf][0];
+    const float* dlt_s = &rowv[buf][BM];
+
+    // S, dP for 2 query blocks of 32 rows x this wave's 32 keys.
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      s[b] = f32x16{};
+      dp[b] = f32x16{};
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        s[b] = f32x16{};
-        dp[b] = f32x16{};
+        const int off = (b * 32 + li) * RS + (16 * ks + 8 * hh);
+        const bf16x8 aq = ld16(Qs + off);
+        const bf16x8 ad = ld16(Ds + off);
+        s[b] = mfma32(aq, kf[ks], s[b]);
+        dp[b] = mfma32(ad, vf[ks], dp[b]);
       }
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const bf16x8 aq = ld16(Qs + (b * 32 + li) * ST + 16 * ks + 8 * hh);
-          const bf16x8 ad = ld16(Ds + (b * 32 + li) * ST + 16 * ks + 8 * hh);
-          s[b] = mfma32(aq, kf[ks], s[b]);
-          dp[b] = mfma32(ad, vf[ks], dp[b]);
-        }
 
-      // P and dS; register r of block b holds query row b*32 + 8(r/4) + 4hh + r%4.
-      f32x16 ds[2];
+    // P and dS; register r of block b holds query row b*32 + 8(r/4) + 4hh + r%4.
+    f32x16 ds[2];
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int rr = b * 32 + 8 * rg + 4 * hh;
-          const float4 l4 = *reinterpret_cast<const float4*>(lse_s + rr);
-          const float4 d4 = *reinterpret_cast<const float4*>(dlt_s + rr);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv_[4] = {d4.x, d4.y, d4.z, d4.w};
+      for (int rg = 0; rg < 4; ++rg) {
+        const int rr = b * 32 + 8 * rg + 4 * hh;
+        const float4 l4 = *reinterpret_cast<const float4*>(lse_s + rr);
+        const float4 d4 = *reinterpret_cast<const float4*>(dlt_s + rr);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv_[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const int r = 4 * rg + x;
-            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], P.scale_log2, -lv[x]));
-            if (partial && !((mask_s[(rr + x) * 4 + w] >> li) & 1u)) pv = 0.f;
-            s[b][r] = pv;
-            ds[b][r] = pv * (dp[b][r] - dv_[x]);
-          }
+        for (int x = 0; x < 4; ++x) {
+          const int r = 4 * rg + x;
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], P.scale_log2, -lv[x]));
+          if (partial && !((mask_s[(rr + x) * 4 + w] >> li) & 1u)) pv = 0.f;
+          s[b][r] = pv;
+          ds[b][r] = pv * (dp[b][r] - dv_[x]);
         }
+      }
 
-      // dV += P^T dO and dK += dS^T Q over the 64 query rows (4 k-steps of 16).
-      // Contraction element e of lane half hh in k-step (b, t2) is query row
-      // b*32 + 16 t2 + 8(e/4) + 4hh + e%4 -- registers 8 t2 .. 8 t2 + 7.
+    // dV += P^T dO and dK += dS^T Q over the 64 query rows (4 k-steps of 16).
+    // Contraction element e of lane half hh in k-step (b, t2) is query row
+    // b*32 + 16 t2 + 8(e/4) + 4hh + e%4 -- registers 8 t2 .. 8 t2 + 7.
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const bf16x8 pa = to_bf16x8(s[b], 8 * t2);
-          const bf16x8 sa = to_bf16x8(ds[b], 8 * t2);
-          const int qrow = b * 32 + 16 * t2 + 4 * hh + tr_row(lane);
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const bf16x8 pa = to_bf16x8(s[b], 8 * t2);
+        const bf16x8 sa = to_bf16x8(ds[b], 8 * t2);
+        const int qrow = b * 32 + 16 * t2 + 4 * hh + tr_row(lane);
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const int col = db * 32 + tr_col(lane);
-            const bf16x8 bd = ld_tr8(Ds + qrow * ST + col, Ds + (qrow + 8) * ST + col);
-            const bf16x8 bq = ld_tr8(Qs + qrow * ST + col, Qs + (qrow + 8) * ST + col);
-            dva[db] = mfma32(pa, bd, dva[db]);
-            dka[db] = mfma32(sa, bq, dka[db]);
-          }
+        for (int db = 0; db < NDB; ++db) {
+          const int col = db * 32 + tr_col(lane);
+          const bf16x8 bd = ld_tr8(Ds + (qrow) * RS + (col), Ds + (qrow + 8) * RS + (col));
+          const bf16x8 bq = ld_tr8(Qs + (qrow) * RS + (col), Qs + (qrow + 8) * RS + (col));
+          dva[db] = mfma32(pa, bd, dva[db]);
+          dka[db] = mfma32(sa, bq, dka[db]);
         }
-    }
+      }
+    cur = nxt;
   }
 
   // dK, dV: lane holds column d = db*32 + li of key rows 8(r/4) + 4hh + r%4 of the wave's 32 keys.
@@ -367,7 +368,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
 
 hipError_t launch_bwd(const AttnParams& Pq, const AttnParams& Pkv, int D, int nq_items, int nkv_items,
                       uint32_t phases, hipStream_t stream) {
-  const int64_t nrows = (int64_t)Pq.Tq * Pq.Hq;
+  const int64_t nrows = (int64_t)Pq.Tq_pad * Pq.Hq;
   if ((phases & MAD_BWD_DELTA) && nrows > 0) {
     const int64_t threads = nrows * (D / 8);
     const int nb = (int)((threads + 255) / 256);

@@ -8,15 +8,17 @@
 //
 // Work decomposition: one workgroup per (query head, 128-row query tile), two
 // wave64s of 64 rows each.  The workgroup walks the query tile's list of
-// non-EMPTY 64-key tiles; K and V tiles are staged through LDS (the next
-// tile's global loads are in flight while the current one is computed).  Per
-// key tile each wave
+// non-EMPTY 64-key tiles.  K and V tiles reach LDS by direct global->LDS
+// loads into a double buffer: the loads of tile t+1 are issued right after
+// the barrier that opens tile t, so they overlap tile t's arithmetic and no
+// registers are spent on staging.  Per key tile each wave
 //   1. forms S^T = K Q^T (keys x queries) with bf16 MFMA; each lane then holds
 //      one query row, so the row max and row sum stay in the lane (plus one
 //      permlane32 swap with the other half-wave);
 //   2. masks PARTIAL tiles (and the ragged last key tile) with -inf;
-//   3. updates the online softmax in the exp2 domain (running max m, sum l,
-//      rescale factor alpha = exp2(m_old - m_new));
+//   3. updates the online softmax in the exp2 domain (running max m, sum l);
+//      the accumulator is rescaled by exp2(m_old - m_new) only when some row
+//      of the wave raised its max;
 //   4. accumulates O^T += V^T P^T with P^T taken straight from registers as
 //      the MFMA B operand and V^T read transposed from LDS.
 #include "kernel_common.hpp"
@@ -25,11 +27,8 @@ namespace mad {
 
 template <int D>
 __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
-  constexpr int BM = BM0, BN = BN0, ST = lds_stride<D>(), NKS = D / 16, NDB = D / 32;
-  constexpr int CPR = D / 8;            // 16-byte chunks per row
-  constexpr int CH = BN * CPR / 128;    // chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) bf16 Ks[BN * ST];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[BN * ST];
+  constexpr int BM = BM0, BN = BN0, NKS = D / 16, NDB = D / 32, TILE = tile_elems<D>(), RS = tile_rs<D>();
+  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // K0 V0 K1 V1
 
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int e = L % P.R, t_ = L / P.R;
@@ -40,17 +39,24 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, li = lane & 31;
   const int row_base = qt * BM + w * 64;
 
+  const int32_t* ptr = P.t.ptr + (int64_t)mg * (P.t.nmajor + 1);
+  const int beg = ptr[qt], end = ptr[qt + 1];
+  const bf16* kg = P.k + (int64_t)g * P.k_head;
+  const bf16* vg = P.v + (int64_t)g * P.v_head;
+  auto issue = [&](int kt, int buf) {
+    tile_load_async<D, 2, true>(smem + (2 * buf) * TILE, kg, P.k_tok, kt * BN, P.Tk, w, lane);
+    tile_load_async<D, 2, false>(smem + (2 * buf + 1) * TILE, vg, P.v_tok, kt * BN, P.Tk, w, lane);
+  };
+  if (beg < end) issue(P.t.ent[beg] & 0x7fffffff, 0);
+
   // Q as the B operand of S^T = K Q^T: lane holds Q[row][16ks + 8hh .. +8].
   bf16x8 qf[2][NKS];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int row = row_base + b * 32 + li;
-    const bf16* src = P.q + (int64_t)row * P.q_tok + (int64_t)h * P.q_head + 8 * hh;
+    const bf16* src = P.q + (int64_t)min(row, P.Tq - 1) * P.q_tok + (int64_t)h * P.q_head + 8 * hh;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      if (row < P.Tq) qf[b][ks] = ld16(src + 16 * ks);
-      else qf[b][ks] = bf16x8{};
-    }
+    for (int ks = 0; ks < NKS; ++ks) qf[b][ks] = ld16(src + 16 * ks);
   }
 
   f32x16 acc[NDB][2];
@@ -60,42 +66,30 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
     for (int b = 0; b < 2; ++b) acc[db][b] = f32x16{};
   float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
 
-  const int32_t* ptr = P.t.ptr + (int64_t)mg * (P.t.nmajor + 1);
-  const int beg = ptr[qt], end = ptr[qt + 1];
-
-  u32x4 kr[CH], vr[CH];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int id = tid + 128 * c, row = id / CPR, col = (id % CPR) * 8;
-      const int key = kt * BN + row;
-      if (key < P.Tk) {
-        kr[c] = gld16(P.k + (int64_t)key * P.k_tok + (int64_t)g * P.k_head + col);
-        vr[c] = gld16(P.v + (int64_t)key * P.v_tok + (int64_t)g * P.v_head + col);
-      } else {
-        kr[c] = u32x4{};
-        vr[c] = u32x4{};
-      }
-    }
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int id = tid + 128 * c, row = id / CPR, col = (id % CPR) * 8;
-      st16(Ks + ((row & 32) | swap23(row & 31)) * ST + col, kr[c]);
-      st16(Vs + row * ST + col, vr[c]);
-    }
-  };
-
-  if (beg < end) gload(P.t.ent[beg] & 0x7fffffff);
   for (int it = beg; it < end; ++it) {
+    const int buf = (it - beg) & 1;
     const uint32_t ent = (uint32_t)P.t.ent[it];
     const int kt = (int)(ent & 0x7fffffffu);
     const bool partial = (ent & ENT_PARTIAL) != 0;
+    wait_vmem();
     __syncthreads();
-    lstore();
-    __syncthreads();
-    if (it + 1 < end) gload(P.t.ent[it + 1] & 0x7fffffff);
+    if (it + 1 < end) issue(P.t.ent[it + 1] & 0x7fffffff, buf ^ 1);
+    const bf16* Ks = smem + (2 * buf) * TILE;
+    const bf16* Vs = smem + (2 * buf + 1) * TILE;
+
+    // Allowed-key masks of this lane's two rows (PARTIAL and ragged tiles only),
+    // evaluated before the scores are live.
+    const bool masked = partial || (kt + 1) * BN > P.Tk;
+    uint32_t mbits[2][2];
+    if (masked) {
+      const int aux = partial ? P.t.ent_aux[it] : -1;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          mbits[b][kb] = keymask32(P.m, aux, mg, partial, row_base + b * 32 + li, kt * BN + kb * 32);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
     // 1. S^T for 2 key blocks x 2 query blocks.
     f32x16 s[2][2];
@@ -107,30 +101,27 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = ld16(Ks + (kb * 32 + li) * ST + 16 * ks + 8 * hh);
+        const bf16x8 a = ld16(Ks + (kb * 32 + li) * RS + (16 * ks + 8 * hh));
 #pragma unroll
         for (int b = 0; b < 2; ++b) s[kb][b] = mfma32(a, qf[b][ks], s[kb][b]);
       }
 
     // 2. Mask.
-    if (partial || (kt + 1) * BN > P.Tk) {
-      const int aux = partial ? P.t.ent_aux[it] : -1;
+    if (masked) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int row = row_base + b * 32 + li;
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const uint32_t bits = keymask32(P.m, aux, mg, partial, row, kt * BN + kb * 32);
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int off = 16 * (r >> 3) + 8 * hh + (r & 7);
-            if (!((bits >> off) & 1u)) s[kb][b][r] = -INFINITY;
+            if (!((mbits[b][kb] >> off) & 1u)) s[kb][b][r] = -INFINITY;
           }
-        }
-      }
     }
 
     // 3. Online softmax (exp2 domain).
+    float mnew[2], alpha[2];
+    bool grew = false;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       float mx = -INFINITY;
@@ -139,10 +130,14 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][b][r]);
       mx = pair_max(mx);
-      const float mnew = fmaxf(mrow[b], mx * P.scale_log2);
-      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(mrow[b] - muse);
-      mrow[b] = mnew;
+      mnew[b] = fmaxf(mrow[b], mx * P.scale_log2);
+      grew |= mnew[b] > mrow[b];
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const float muse = (mnew[b] == -INFINITY) ? 0.f : mnew[b];
+      alpha[b] = __builtin_amdgcn_exp2f(mrow[b] - muse);
+      mrow[b] = mnew[b];
       float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -152,13 +147,18 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
           s[kb][b][r] = pv;
           ls += pv;
         }
-      lrow[b] = lrow[b] * alpha + ls;
+      lrow[b] = lrow[b] * alpha[b] + ls;
+    }
+    if (__ballot(grew)) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][b][r] *= alpha;
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][b][r] *= alpha[b];
     }
 
+    __builtin_amdgcn_sched_barrier(0);
     // 4. O^T += V^T P^T.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const int vcol = db * 32 + tr_col(lane);
-          const bf16x8 a = ld_tr8(Vs + vrow * ST + vcol, Vs + (vrow + 4) * ST + vcol);
+          const bf16x8 a = ld_tr8(Vs + (vrow) * RS + (vcol), Vs + (vrow + 4) * RS + (vcol));
 #pragma unroll
           for (int b = 0; b < 2; ++b) acc[db][b] = mfma32(a, pb[b], acc[db][b]);
         }

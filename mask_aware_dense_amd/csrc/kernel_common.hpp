@@ -29,12 +29,6 @@ typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
-// LDS row stride (elements) of a [rows][D] bf16 tile: the padding keeps both
-// the 16-byte row reads of 16 consecutive rows and the 4-row transposed reads
-// on distinct banks of the 64-bank LDS (stride 76 dwords for D=128, 36 for D=64).
-template <int D>
-constexpr int lds_stride() { return D == 128 ? 152 : 72; }
-
 // Everything a kernel needs about one attention call.
 struct AttnParams {
   const bf16* q;
@@ -45,7 +39,9 @@ struct AttnParams {
   const bf16* o_in;   // backward: forward output
   const bf16* d_o;    // backward: upstream gradient (packed [Tq, Hq, D])
   const float* lse_in;
-  float* delta;       // backward: rowsum(dO * O), [Hq, Tq]
+  float* delta;       // backward: rowsum(dO * O), [Hq, Tq_pad]
+  float* lse2;        // backward: LSE * log2(e), +inf for empty / padded rows, [Hq, Tq_pad]
+  int32_t Tq_pad;     // Tq rounded up to a multiple of 128
   bf16* dq;
   bf16* dk;
   bf16* dv;
@@ -66,8 +62,6 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ bf16x8 ld16(const bf16* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
-__device__ __forceinline__ void st16(bf16* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
-__device__ __forceinline__ u32x4 gld16(const bf16* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 // Two transposed 4-element reads stacked into one 8-element MFMA operand.
 // row0 / row1 address the LDS rows of elements 0..3 and 4..7.
@@ -110,6 +104,58 @@ __device__ __forceinline__ float pair_sum(float x) {
 // next MFMA's contraction operand.
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
+// LDS tiles are [64 rows][D] bf16 images with padded rows: the row stride is
+// RS = D + pad elements, chosen so both access patterns of the kernels fall on
+// distinct banks of the 64-bank LDS (16 chunks of 16 bytes per pass):
+//   (A) 16 consecutive rows reading the same 16-byte column chunk (MFMA
+//       operand rows): stride 76 dwords (D=128) or 36 dwords (D=64) puts the
+//       16 rows on 16 distinct 4-bank groups;
+//   (B) 4 consecutive rows reading 32 contiguous bytes (transposed operand
+//       reads): rows start 12 (D=128) or 36 (D=64) dwords apart mod 64, so the
+//       four 8-bank windows do not overlap.
+// Padding keeps every address affine in the row and column, so operand reads
+// use immediate offsets from one per-lane base.
+template <int D>
+constexpr int tile_rs() { return D == 128 ? 152 : 72; }
+template <int D>
+constexpr int tile_elems() { return 64 * tile_rs<D>(); }
+
+// Direct global -> LDS copy of 16 bytes per lane (gfx950
+// global_load_lds_dwordx4): lane l of the wave writes LDS bytes
+// [lds_base + 16 l, +16).  lds_base must be wave-uniform.
+__device__ __forceinline__ void g2lds16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+// Wait until this wave's outstanding vector-memory loads (including direct
+// LDS loads) have completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Storage row p of a tile holds tensor row tile_row(p): p itself, or swap23
+// within 32-row blocks for tiles read as the score MFMA's A operand.
+__device__ __forceinline__ int tile_row(int p, bool perm) { return perm ? ((p & 32) | swap23(p & 31)) : p; }
+
+// Issue the direct loads of a 64-row tile.  A direct load writes 64
+// consecutive 16-byte slots of LDS per wave instruction, so the padded tile
+// image (64 * RS / 8 slots, RS / 8 per row) takes RS / 8 instructions; slot s
+// holds chunk s % (RS/8) of storage row s / (RS/8), and the pad slots of a row
+// repeat its first chunk (never read).  Storage row p receives tensor row
+// r0 + tile_row(p); rows at or past T are clamped to T - 1 (callers mask
+// those rows, so their values only need to be finite).  g points at the
+// tensor's head; tok is its token stride.  The NW waves of the workgroup
+// take instructions w, w + NW, ...
+template <int D, int NW, bool PERM>
+__device__ __forceinline__ void tile_load_async(bf16* lds, const bf16* g, int64_t tok, int r0, int T, int w,
+                                                int lane) {
+  constexpr int CPR = D / 8, SPR = tile_rs<D>() / 8, NINS = SPR;  // data chunks / slots per row / instructions
+#pragma unroll
+  for (int ii = w; ii < NINS; ii += NW) {
+    const int s = ii * 64 + lane;
+    const int p = s / SPR, c = s % SPR;
+    const int row = min(r0 + tile_row(p, PERM), T - 1);
+    g2lds16(g + (int64_t)row * tok + (c < CPR ? c : 0) * 8, lds + ii * 512);
+  }
+}
+
 // Block index remap so that 8 consecutive logical work items (the query
 // heads of one GQA group at one tile) land on the same XCD: workgroups are
 // dispatched round-robin over the 8 XCDs, each with its own L2.
@@ -131,7 +177,8 @@ __device__ __forceinline__ uint32_t range_bits(int a, int b) {
 // Allowed keys of query row i among keys [key0, key0 + 32) of a visited tile,
 // as a bitmask (bit j <-> key key0 + j).  FULL tiles allow every in-range
 // key; PARTIAL tiles evaluate the mask source: the tile's slice list (SLICES)
-// or the block keep bitmap (BLOCKS).  Keys >= Tk are never allowed.
+// or the block keep bitmap (BLOCKS).  Keys >= Tk and rows >= Tq are never
+// allowed.
 __device__ __forceinline__ uint32_t keymask32(const MaskDev& m, int32_t aux, int32_t grp, bool partial, int i,
                                               int key0) {
   uint32_t bits;
@@ -165,6 +212,7 @@ __device__ __forceinline__ uint32_t keymask32(const MaskDev& m, int32_t aux, int
   }
   const int nvalid = m.Tk - key0;
   if (nvalid < 32) bits &= (nvalid <= 0) ? 0u : ((1u << nvalid) - 1u);
+  if (i >= m.Tq) bits = 0u;
   return bits;
 }
 
