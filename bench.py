@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=96, help="query rows in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fwd-only", action="store_true", help="time only the forward (profiling aid)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (HBM byte-counter calibration) and exit")
     return ap.parse_args()
 
 
@@ -85,6 +87,15 @@ def main():
                           "detail": "no collectives or sharding are built; see the design notes on sharding"}))
         sys.exit(2)
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}))
+        return
     import mask_aware_dense_amd as mad
     from mad_inputs import grad_out, qkv
     from oracle import masks as M

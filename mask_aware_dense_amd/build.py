@@ -33,6 +33,10 @@ def flags():
         # packed fp32 VALU forms stay off in every device build
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", os.path.join(ROOT, "include"), "-Wno-unused-result",
+        # MFMA results in arch VGPRs: the score tiles feed VALU softmax code
+        # directly, and the register allocator then keeps every kernel
+        # spill-free (measured: forward 58.9 -> 22.7 ms at 32K causal)
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
     ]
 
 

@@ -80,9 +80,12 @@ __global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
   const int beg = ptr[qt], end = ptr[qt + 1];
   const bf16* kg = P.k + (int64_t)g * P.k_head;
   const bf16* vg = P.v + (int64_t)g * P.v_head;
+  TileLoader<D, 2, true> kload, vload;
+  kload.init(P.k_tok, w, lane);
+  vload.init(P.v_tok, w, lane);
   auto issue = [&](int kt, int buf) {
-    tile_load_async<D, 2, true>(smem + (2 * buf) * TILE, kg, P.k_tok, kt * BN, P.Tk, w, lane);
-    tile_load_async<D, 2, true>(smem + (2 * buf + 1) * TILE, vg, P.v_tok, kt * BN, P.Tk, w, lane);
+    kload.issue(smem + (2 * buf) * TILE, kg, P.k_tok, kt * BN, P.Tk, w, lane);
+    vload.issue(smem + (2 * buf + 1) * TILE, vg, P.v_tok, kt * BN, P.Tk, w, lane);
   };
   if (beg < end) issue(P.t.ent[beg] & 0x7fffffff, 0);
 
@@ -252,12 +255,14 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
   auto settle = [&](Cursor& c) {  // move past exhausted heads
     while (c.it >= c.end && c.e + 1 < P.R) head_list(c.e + 1, c);
   };
+  TileLoader<D, 4, false> qload, dload;
+  qload.init(P.q_tok, w, lane);
+  dload.init((int64_t)P.Hq * D, w, lane);
   auto issue = [&](const Cursor& c, int buf) {
     const int hx = g * P.R + c.e;
     const int q0 = (P.t.ent[c.it] & 0x7fffffff) * BM;
-    tile_load_async<D, 4, false>(smem + (2 * buf) * TILE, P.q + (int64_t)hx * P.q_head, P.q_tok, q0, P.Tq, w, lane);
-    tile_load_async<D, 4, false>(smem + (2 * buf + 1) * TILE, P.d_o + (int64_t)hx * D, (int64_t)P.Hq * D, q0, P.Tq,
-                                 w, lane);
+    qload.issue(smem + (2 * buf) * TILE, P.q + (int64_t)hx * P.q_head, P.q_tok, q0, P.Tq, w, lane);
+    dload.issue(smem + (2 * buf + 1) * TILE, P.d_o + (int64_t)hx * D, (int64_t)P.Hq * D, q0, P.Tq, w, lane);
     if (w == 0 && lane < 32) {
       const float* src = (lane < 16 ? P.lse2 : P.delta) + (int64_t)hx * P.Tq_pad + q0 + 4 * (lane & 15);
       g2lds16(src, &rowv[buf][0]);

@@ -16,9 +16,9 @@
 //      one query row, so the row max and row sum stay in the lane (plus one
 //      permlane32 swap with the other half-wave);
 //   2. masks PARTIAL tiles (and the ragged last key tile) with -inf;
-//   3. updates the online softmax in the exp2 domain (running max m, sum l);
-//      the accumulator is rescaled by exp2(m_old - m_new) only when some row
-//      of the wave raised its max;
+//   3. updates the online softmax in the exp2 domain against a lagging
+//      reference max that moves (with a rescale of the accumulator) only when
+//      a row's max grows by more than 2^8;
 //   4. accumulates O^T += V^T P^T with P^T taken straight from registers as
 //      the MFMA B operand and V^T read transposed from LDS.
 #include "kernel_common.hpp"
@@ -43,9 +43,13 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
   const int beg = ptr[qt], end = ptr[qt + 1];
   const bf16* kg = P.k + (int64_t)g * P.k_head;
   const bf16* vg = P.v + (int64_t)g * P.v_head;
+  TileLoader<D, 2, true> kload;
+  TileLoader<D, 2, false> vload;
+  kload.init(P.k_tok, w, lane);
+  vload.init(P.v_tok, w, lane);
   auto issue = [&](int kt, int buf) {
-    tile_load_async<D, 2, true>(smem + (2 * buf) * TILE, kg, P.k_tok, kt * BN, P.Tk, w, lane);
-    tile_load_async<D, 2, false>(smem + (2 * buf + 1) * TILE, vg, P.v_tok, kt * BN, P.Tk, w, lane);
+    kload.issue(smem + (2 * buf) * TILE, kg, P.k_tok, kt * BN, P.Tk, w, lane);
+    vload.issue(smem + (2 * buf + 1) * TILE, vg, P.v_tok, kt * BN, P.Tk, w, lane);
   };
   if (beg < end) issue(P.t.ent[beg] & 0x7fffffff, 0);
 
@@ -119,9 +123,15 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
           }
     }
 
-    // 3. Online softmax (exp2 domain).
-    float mnew[2], alpha[2];
-    bool grew = false;
+    // 3. Online softmax (exp2 domain) with a lagging reference max: each row
+    // keeps a reference m_ref and forms p = exp2(s*c - m_ref).  m_ref moves up
+    // (and the accumulator and sum are rescaled by exp2(m_old - m_new)) only
+    // when the tile's max exceeds m_ref by more than RESCALE_SLACK, so p stays
+    // below 2^RESCALE_SLACK and the rescale is rare.  The result is exact: O
+    // and l share the same reference, and LSE = m_ref + log2(l).
+    constexpr float RESCALE_SLACK = 8.f;
+    float tmax[2];
+    bool need = false;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       float mx = -INFINITY;
@@ -129,15 +139,25 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][b][r]);
-      mx = pair_max(mx);
-      mnew[b] = fmaxf(mrow[b], mx * P.scale_log2);
-      grew |= mnew[b] > mrow[b];
+      tmax[b] = pair_max(mx) * P.scale_log2;
+      need |= tmax[b] > mrow[b] + RESCALE_SLACK;
+    }
+    if (__ballot(need)) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const float mnew = fmaxf(mrow[b], tmax[b]);
+        const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrow[b] - mnew);
+        mrow[b] = mnew;
+        lrow[b] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][b][r] *= alpha;
+      }
     }
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const float muse = (mnew[b] == -INFINITY) ? 0.f : mnew[b];
-      alpha[b] = __builtin_amdgcn_exp2f(mrow[b] - muse);
-      mrow[b] = mnew[b];
+      const float muse = (mrow[b] == -INFINITY) ? 0.f : mrow[b];
       float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -147,15 +167,7 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
           s[kb][b][r] = pv;
           ls += pv;
         }
-      lrow[b] = lrow[b] * alpha[b] + ls;
-    }
-    if (__ballot(grew)) {
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][b][r] *= alpha[b];
+      lrow[b] += ls;
     }
 
     __builtin_amdgcn_sched_barrier(0);

@@ -134,27 +134,54 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // within 32-row blocks for tiles read as the score MFMA's A operand.
 __device__ __forceinline__ int tile_row(int p, bool perm) { return perm ? ((p & 32) | swap23(p & 31)) : p; }
 
-// Issue the direct loads of a 64-row tile.  A direct load writes 64
-// consecutive 16-byte slots of LDS per wave instruction, so the padded tile
-// image (64 * RS / 8 slots, RS / 8 per row) takes RS / 8 instructions; slot s
-// holds chunk s % (RS/8) of storage row s / (RS/8), and the pad slots of a row
+// Direct loads of a 64-row tile.  A direct load writes 64 consecutive
+// 16-byte slots of LDS per wave instruction, so the padded tile image
+// (RS / 8 slots per row, 64 rows) takes RS / 8 instructions; slot s holds
+// chunk s % (RS/8) of storage row s / (RS/8), and the pad slots of a row
 // repeat its first chunk (never read).  Storage row p receives tensor row
-// r0 + tile_row(p); rows at or past T are clamped to T - 1 (callers mask
-// those rows, so their values only need to be finite).  g points at the
-// tensor's head; tok is its token stride.  The NW waves of the workgroup
-// take instructions w, w + NW, ...
+// r0 + tile_row(p).  The NW waves of a workgroup take instructions
+// w, w + NW, ...  Each lane's source offset within a tile is the same for
+// every tile, so it is computed once (init) and a tile then costs one
+// wave-uniform base per instruction (issue).  A tile reaching past row T
+// (the ragged last tile) clamps its rows to T - 1; callers mask those rows,
+// so their values only need to be finite.
 template <int D, int NW, bool PERM>
-__device__ __forceinline__ void tile_load_async(bf16* lds, const bf16* g, int64_t tok, int r0, int T, int w,
-                                                int lane) {
-  constexpr int CPR = D / 8, SPR = tile_rs<D>() / 8, NINS = SPR;  // data chunks / slots per row / instructions
+struct TileLoader {
+  static constexpr int SPR = tile_rs<D>() / 8, CPR = D / 8, NI = (SPR + NW - 1) / NW;
+  uint32_t off[NI];  // byte offset of this lane's source chunk from the tile's first row
+
+  __device__ __forceinline__ void init(int64_t tok, int w, int lane) {
 #pragma unroll
-  for (int ii = w; ii < NINS; ii += NW) {
-    const int s = ii * 64 + lane;
-    const int p = s / SPR, c = s % SPR;
-    const int row = min(r0 + tile_row(p, PERM), T - 1);
-    g2lds16(g + (int64_t)row * tok + (c < CPR ? c : 0) * 8, lds + ii * 512);
+    for (int i = 0; i < NI; ++i) {
+      const int s = (i * NW + w) * 64 + lane;
+      const int p = s / SPR, c = s % SPR;
+      off[i] = (uint32_t)(((int64_t)tile_row(p, PERM) * tok + (c < CPR ? c : 0) * 8) * 2);
+    }
   }
-}
+  // g: the tensor's head; tok: its token stride (elements).
+  __device__ __forceinline__ void issue(bf16* lds, const bf16* g, int64_t tok, int r0, int T, int w,
+                                        int lane) const {
+    if (r0 + 64 <= T) {
+      const char* base = reinterpret_cast<const char*>(g + (int64_t)r0 * tok);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int ii = i * NW + w;
+        if (ii < SPR) g2lds16(base + off[i], lds + ii * 512);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int ii = i * NW + w;
+        if (ii < SPR) {
+          const int s = ii * 64 + lane;
+          const int p = s / SPR, c = s % SPR;
+          const int row = min(r0 + tile_row(p, PERM), T - 1);
+          g2lds16(g + (int64_t)row * tok + (c < CPR ? c : 0) * 8, lds + ii * 512);
+        }
+      }
+    }
+  }
+};
 
 // Block index remap so that 8 consecutive logical work items (the query
 // heads of one GQA group at one tile) land on the same XCD: workgroups are
