@@ -64,8 +64,10 @@ __global__ __launch_bounds__(256) void delta_kernel(const AttnParams P) {
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
-  constexpr int BM = BM0, BN = BN0, NKS = D / 16, NDB = D / 32, TILE = tile_elems<D>(), RS = tile_rs<D>();
-  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // K0 V0 K1 V1
+  constexpr int BM = BM0, BN = BN0, NKS = D / 16, NDB = D / 32;
+  constexpr int KRS = tile_rs<D, TILE_MIXED>(), KT = tile_elems<D, TILE_MIXED>();
+  constexpr int VRS = tile_rs<D, TILE_ROWS>(), VT = tile_elems<D, TILE_ROWS>();
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * (KT + VT)];  // K0 V0 K1 V1
 
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int e = L % P.R, t_ = L / P.R;
@@ -80,12 +82,13 @@ __global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
   const int beg = ptr[qt], end = ptr[qt + 1];
   const bf16* kg = P.k + (int64_t)g * P.k_head;
   const bf16* vg = P.v + (int64_t)g * P.v_head;
-  TileLoader<D, 2, true> kload, vload;
+  TileLoader<D, TILE_MIXED, 2, true> kload;
+  TileLoader<D, TILE_ROWS, 2, true> vload;
   kload.init(P.k_tok, w, lane);
   vload.init(P.v_tok, w, lane);
   auto issue = [&](int kt, int buf) {
-    kload.issue(smem + (2 * buf) * TILE, kg, P.k_tok, kt * BN, P.Tk, w, lane);
-    vload.issue(smem + (2 * buf + 1) * TILE, vg, P.v_tok, kt * BN, P.Tk, w, lane);
+    kload.issue(smem + buf * (KT + VT), kg, P.k_tok, kt * BN, P.Tk, w, lane);
+    vload.issue(smem + buf * (KT + VT) + KT, vg, P.v_tok, kt * BN, P.Tk, w, lane);
   };
   if (beg < end) issue(P.t.ent[beg] & 0x7fffffff, 0);
 
@@ -122,8 +125,8 @@ __global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
     wait_vmem();
     __syncthreads();
     if (it + 1 < end) issue(P.t.ent[it + 1] & 0x7fffffff, buf ^ 1);
-    const bf16* Ks = smem + (2 * buf) * TILE;
-    const bf16* Vs = smem + (2 * buf + 1) * TILE;
+    const bf16* Ks = smem + buf * (KT + VT);
+    const bf16* Vs = Ks + KT;
 
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -135,9 +138,8 @@ __global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
       }
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const int off = (kb * 32 + li) * RS + (16 * ks + 8 * hh);
-        const bf16x8 ak = ld16(Ks + off);
-        const bf16x8 av = ld16(Vs + off);
+        const bf16x8 ak = ld16(Ks + (kb * 32 + li) * KRS + 16 * ks + 8 * hh);
+        const bf16x8 av = ld16(Vs + (kb * 32 + li) * VRS + 16 * ks + 8 * hh);
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
           s[b] = mfma32(ak, qf[b][ks], s[b]);
@@ -173,7 +175,7 @@ __global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const int kcol = db * 32 + tr_col(lane);
-          const bf16x8 a = ld_tr8(Ks + (krow) * RS + (kcol), Ks + (krow + 8) * RS + (kcol));
+          const bf16x8 a = ld_tr8(Ks + krow * KRS + kcol, Ks + (krow + 8) * KRS + kcol);
 #pragma unroll
           for (int b = 0; b < 2; ++b) acc[db][b] = mfma32(a, sb[b], acc[db][b]);
         }
@@ -210,7 +212,8 @@ __global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
-  constexpr int BM = BM1, BN = BN1, NKS = D / 16, NDB = D / 32, TILE = tile_elems<D>(), RS = tile_rs<D>();
+  constexpr int BM = BM1, BN = BN1, NKS = D / 16, NDB = D / 32;
+  constexpr int TILE = tile_elems<D, TILE_MIXED>(), RS = tile_rs<D, TILE_MIXED>();
   __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];   // Q0 dO0 Q1 dO1
   __shared__ __attribute__((aligned(256))) float rowv[2][2 * BM];  // per buffer: lse2[64], delta[64]
   __shared__ uint32_t mask_s[BM * 4];
@@ -255,7 +258,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
   auto settle = [&](Cursor& c) {  // move past exhausted heads
     while (c.it >= c.end && c.e + 1 < P.R) head_list(c.e + 1, c);
   };
-  TileLoader<D, 4, false> qload, dload;
+  TileLoader<D, TILE_MIXED, 4, false> qload, dload;
   qload.init(P.q_tok, w, lane);
   dload.init((int64_t)P.Hq * D, w, lane);
   auto issue = [&](const Cursor& c, int buf) {

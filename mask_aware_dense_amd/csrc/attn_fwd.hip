@@ -27,8 +27,10 @@ namespace mad {
 
 template <int D>
 __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
-  constexpr int BM = BM0, BN = BN0, NKS = D / 16, NDB = D / 32, TILE = tile_elems<D>(), RS = tile_rs<D>();
-  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // K0 V0 K1 V1
+  constexpr int BM = BM0, BN = BN0, NKS = D / 16, NDB = D / 32;
+  constexpr int KRS = tile_rs<D, TILE_ROWS>(), KT = tile_elems<D, TILE_ROWS>();
+  constexpr int VRS = tile_rs<D, TILE_TR>(), VT = tile_elems<D, TILE_TR>();
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * (KT + VT)];  // K0 V0 K1 V1
 
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int e = L % P.R, t_ = L / P.R;
@@ -43,13 +45,13 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
   const int beg = ptr[qt], end = ptr[qt + 1];
   const bf16* kg = P.k + (int64_t)g * P.k_head;
   const bf16* vg = P.v + (int64_t)g * P.v_head;
-  TileLoader<D, 2, true> kload;
-  TileLoader<D, 2, false> vload;
+  TileLoader<D, TILE_ROWS, 2, true> kload;
+  TileLoader<D, TILE_TR, 2, false> vload;
   kload.init(P.k_tok, w, lane);
   vload.init(P.v_tok, w, lane);
   auto issue = [&](int kt, int buf) {
-    kload.issue(smem + (2 * buf) * TILE, kg, P.k_tok, kt * BN, P.Tk, w, lane);
-    vload.issue(smem + (2 * buf + 1) * TILE, vg, P.v_tok, kt * BN, P.Tk, w, lane);
+    kload.issue(smem + buf * (KT + VT), kg, P.k_tok, kt * BN, P.Tk, w, lane);
+    vload.issue(smem + buf * (KT + VT) + KT, vg, P.v_tok, kt * BN, P.Tk, w, lane);
   };
   if (beg < end) issue(P.t.ent[beg] & 0x7fffffff, 0);
 
@@ -78,8 +80,8 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
     wait_vmem();
     __syncthreads();
     if (it + 1 < end) issue(P.t.ent[it + 1] & 0x7fffffff, buf ^ 1);
-    const bf16* Ks = smem + (2 * buf) * TILE;
-    const bf16* Vs = smem + (2 * buf + 1) * TILE;
+    const bf16* Ks = smem + buf * (KT + VT);
+    const bf16* Vs = Ks + KT;
 
     // Allowed-key masks of this lane's two rows (PARTIAL and ragged tiles only),
     // evaluated before the scores are live.
@@ -105,13 +107,14 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = ld16(Ks + (kb * 32 + li) * RS + (16 * ks + 8 * hh));
+        const bf16x8 a = ld16(Ks + (kb * 32 + li) * KRS + (16 * ks + 8 * hh));
 #pragma unroll
         for (int b = 0; b < 2; ++b) s[kb][b] = mfma32(a, qf[b][ks], s[kb][b]);
       }
 
-    // 2. Mask.
-    if (masked) {
+    // 2. Mask (a real branch: FULL tiles must not pay for it).
+    if (__builtin_expect(masked, 0)) {
+      asm volatile("" ::: "memory");
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -183,7 +186,7 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const int vcol = db * 32 + tr_col(lane);
-          const bf16x8 a = ld_tr8(Vs + (vrow) * RS + (vcol), Vs + (vrow + 4) * RS + (vcol));
+          const bf16x8 a = ld_tr8(Vs + vrow * VRS + vcol, Vs + (vrow + 4) * VRS + vcol);
 #pragma unroll
           for (int b = 0; b < 2; ++b) acc[db][b] = mfma32(a, pb[b], acc[db][b]);
         }

@@ -104,21 +104,28 @@ __device__ __forceinline__ float pair_sum(float x) {
 // next MFMA's contraction operand.
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-// LDS tiles are [64 rows][D] bf16 images with padded rows: the row stride is
-// RS = D + pad elements, chosen so both access patterns of the kernels fall on
-// distinct banks of the 64-bank LDS (16 chunks of 16 bytes per pass):
-//   (A) 16 consecutive rows reading the same 16-byte column chunk (MFMA
-//       operand rows): stride 76 dwords (D=128) or 36 dwords (D=64) puts the
-//       16 rows on 16 distinct 4-bank groups;
-//   (B) 4 consecutive rows reading 32 contiguous bytes (transposed operand
-//       reads): rows start 12 (D=128) or 36 (D=64) dwords apart mod 64, so the
-//       four 8-bank windows do not overlap.
+// LDS tiles are [64 rows][D] bf16 images with padded rows.  The row stride
+// RS (elements) depends on how a tile is read, because the two read kinds
+// want different bank spreads on the 64-bank LDS (measured with the
+// SQ_LDS_BANK_CONFLICT counter):
+//   ROWS  - 16-byte row reads (MFMA operand rows): 8 lanes per pass read the
+//           same column of 8 consecutive rows; conflict-free when the stride
+//           is 4 mod 8 dwords (272 B for D=128, 144 B for D=64).
+//   TR    - transposed reads (ds_read_b64_tr_b16): 32 lanes per pass read
+//           64 bytes of each of 4 consecutive rows; conflict-free when the
+//           stride is 16 mod 32 dwords (320 B for D=128, 192 B for D=64).
+//   MIXED - both; 304 B (D=128) / 144 B (D=64) keeps row reads conflict-free
+//           and transposed reads at two-way conflicts.
 // Padding keeps every address affine in the row and column, so operand reads
 // use immediate offsets from one per-lane base.
-template <int D>
-constexpr int tile_rs() { return D == 128 ? 152 : 72; }
-template <int D>
-constexpr int tile_elems() { return 64 * tile_rs<D>(); }
+enum TileKind { TILE_ROWS = 0, TILE_TR = 1, TILE_MIXED = 2 };
+template <int D, int KIND>
+constexpr int tile_rs() {
+  return D == 128 ? (KIND == TILE_ROWS ? 136 : KIND == TILE_TR ? 160 : 152)
+                  : (KIND == TILE_TR ? 96 : 72);
+}
+template <int D, int KIND>
+constexpr int tile_elems() { return 64 * tile_rs<D, KIND>(); }
 
 // Direct global -> LDS copy of 16 bytes per lane (gfx950
 // global_load_lds_dwordx4): lane l of the wave writes LDS bytes
@@ -145,9 +152,9 @@ __device__ __forceinline__ int tile_row(int p, bool perm) { return perm ? ((p & 
 // wave-uniform base per instruction (issue).  A tile reaching past row T
 // (the ragged last tile) clamps its rows to T - 1; callers mask those rows,
 // so their values only need to be finite.
-template <int D, int NW, bool PERM>
+template <int D, int KIND, int NW, bool PERM>
 struct TileLoader {
-  static constexpr int SPR = tile_rs<D>() / 8, CPR = D / 8, NI = (SPR + NW - 1) / NW;
+  static constexpr int SPR = tile_rs<D, KIND>() / 8, CPR = D / 8, NI = (SPR + NW - 1) / NW;
   uint32_t off[NI];  // byte offset of this lane's source chunk from the tile's first row
 
   __device__ __forceinline__ void init(int64_t tok, int w, int lane) {
