@@ -73,13 +73,13 @@ __global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
   const int e = L % P.R, t_ = L / P.R;
   const int g = t_ % P.Hkv, rank = t_ / P.Hkv;
   const int h = g * P.R + e;
-  const int qt = P.t.order[rank];
+  const int qt = sld(P.t.order + rank);
   const int mg = h / P.grp_div;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, li = lane & 31;
   const int row_base = qt * BM + w * 64;
 
   const int32_t* ptr = P.t.ptr + (int64_t)mg * (P.t.nmajor + 1);
-  const int beg = ptr[qt], end = ptr[qt + 1];
+  const int beg = sld(ptr + qt), end = sld(ptr + qt + 1);
   const bf16* kg = P.k + (int64_t)g * P.k_head;
   const bf16* vg = P.v + (int64_t)g * P.v_head;
   TileLoader<D, TILE_MIXED, 2, true> kload;
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
     kload.issue(smem + buf * (KT + VT), kg, P.k_tok, kt * BN, P.Tk, w, lane);
     vload.issue(smem + buf * (KT + VT) + KT, vg, P.v_tok, kt * BN, P.Tk, w, lane);
   };
-  if (beg < end) issue(P.t.ent[beg] & 0x7fffffff, 0);
+  if (beg < end) issue(sld(P.t.ent + beg) & 0x7fffffff, 0);
 
   bf16x8 qf[2][NKS], df[2][NKS];
   float lse2[2], dlt[2];
@@ -117,14 +117,25 @@ __global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
 
   for (int it = beg; it < end; ++it) {
     const int buf = (it - beg) & 1;
-    const uint32_t ent = (uint32_t)P.t.ent[it];
+    const uint32_t ent = (uint32_t)sld(P.t.ent + it);
     const int kt = (int)(ent & 0x7fffffffu);
     const bool partial = (ent & ENT_PARTIAL) != 0;
     const bool masked = partial || (kt + 1) * BN > P.Tk;
-    const int aux = partial ? P.t.ent_aux[it] : -1;
     wait_vmem();
     __syncthreads();
-    if (it + 1 < end) issue(P.t.ent[it + 1] & 0x7fffffff, buf ^ 1);
+    // Allowed-key masks (PARTIAL and ragged tiles), evaluated before the next
+    // tile's loads are issued so that the mask table reads never wait behind them.
+    uint32_t mbits[2][2];
+    if (masked) {
+      const int aux = partial ? sld(P.t.ent_aux + it) : -1;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          mbits[kb][b] = keymask32(P.m, aux, mg, partial, row_base + b * 32 + li, kt * BN + kb * 32);
+      wait_vmem();
+    }
+    if (it + 1 < end) issue(sld(P.t.ent + it + 1) & 0x7fffffff, buf ^ 1);
     const bf16* Ks = smem + buf * (KT + VT);
     const bf16* Vs = Ks + KT;
 
@@ -149,7 +160,7 @@ __global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
       if (masked) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-          const uint32_t bits = keymask32(P.m, aux, mg, partial, row_base + b * 32 + li, kt * BN + kb * 32);
+          const uint32_t bits = mbits[kb][b];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int off = 16 * (r >> 3) + 8 * hh + (r & 7);
@@ -219,7 +230,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
   __shared__ uint32_t mask_s[BM * 4];
 
   const int L = blockIdx.x;
-  const int kt = P.t.order[L / P.Hkv];
+  const int kt = sld(P.t.order + L / P.Hkv);
   const int g = L % P.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, li = lane & 31;
   const int key = kt * BN + w * 32 + li;
@@ -252,8 +263,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
   auto head_list = [&](int e, Cursor& c) {
     const int32_t* ptr = P.t.ptr + (int64_t)((g * P.R + e) / P.grp_div) * (P.t.nmajor + 1);
     c.e = e;
-    c.it = ptr[kt];
-    c.end = ptr[kt + 1];
+    c.it = sld(ptr + kt);
+    c.end = sld(ptr + kt + 1);
   };
   auto settle = [&](Cursor& c) {  // move past exhausted heads
     while (c.it >= c.end && c.e + 1 < P.R) head_list(c.e + 1, c);
@@ -263,7 +274,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
   dload.init((int64_t)P.Hq * D, w, lane);
   auto issue = [&](const Cursor& c, int buf) {
     const int hx = g * P.R + c.e;
-    const int q0 = (P.t.ent[c.it] & 0x7fffffff) * BM;
+    const int q0 = (sld(P.t.ent + c.it) & 0x7fffffff) * BM;
     qload.issue(smem + (2 * buf) * TILE, P.q + (int64_t)hx * P.q_head, P.q_tok, q0, P.Tq, w, lane);
     dload.issue(smem + (2 * buf + 1) * TILE, P.d_o + (int64_t)hx * D, (int64_t)P.Hq * D, q0, P.Tq, w, lane);
     if (w == 0 && lane < 32) {
@@ -281,7 +292,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
     const int h = g * P.R + cur.e;
     const int it = cur.it;
     const int mg = h / P.grp_div;
-    const uint32_t ent = (uint32_t)P.t.ent[it];
+    const uint32_t ent = (uint32_t)sld(P.t.ent + it);
     const int qt = (int)(ent & 0x7fffffffu);
     const bool partial = (ent & ENT_PARTIAL) != 0;
     const int q0 = qt * BM;
@@ -290,11 +301,14 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
     settle(nxt);
     wait_vmem();
     __syncthreads();
-    if (nxt.it < nxt.end) issue(nxt, buf ^ 1);
+    // Mask words of a PARTIAL tile are built before the next tiles' loads
+    // are issued, so that the mask table reads never wait behind them.
     if (partial) {
-      mask_s[tid] = keymask32(P.m, P.t.ent_aux[it], mg, true, q0 + (tid >> 2), kt * BN + 32 * (tid & 3));
-      __syncthreads();
+      mask_s[tid] = keymask32(P.m, sld(P.t.ent_aux + it), mg, true, q0 + (tid >> 2), kt * BN + 32 * (tid & 3));
+      wait_vmem();
     }
+    if (nxt.it < nxt.end) issue(nxt, buf ^ 1);
+    if (partial) __syncthreads();
     const bf16* Qs = smem + (2 * buf) * TILE;
     const bf16* Ds = smem + (2 * buf + 1) * TILE;
     const float* lse_s = &rowv[buf][0];

@@ -36,13 +36,13 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
   const int e = L % P.R, t_ = L / P.R;
   const int g = t_ % P.Hkv, rank = t_ / P.Hkv;
   const int h = g * P.R + e;
-  const int qt = P.t.order[rank];
+  const int qt = sld(P.t.order + rank);
   const int mg = h / P.grp_div;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, li = lane & 31;
   const int row_base = qt * BM + w * 64;
 
   const int32_t* ptr = P.t.ptr + (int64_t)mg * (P.t.nmajor + 1);
-  const int beg = ptr[qt], end = ptr[qt + 1];
+  const int beg = sld(ptr + qt), end = sld(ptr + qt + 1);
   const bf16* kg = P.k + (int64_t)g * P.k_head;
   const bf16* vg = P.v + (int64_t)g * P.v_head;
   TileLoader<D, TILE_ROWS, 2, true> kload;
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
     kload.issue(smem + buf * (KT + VT), kg, P.k_tok, kt * BN, P.Tk, w, lane);
     vload.issue(smem + buf * (KT + VT) + KT, vg, P.v_tok, kt * BN, P.Tk, w, lane);
   };
-  if (beg < end) issue(P.t.ent[beg] & 0x7fffffff, 0);
+  if (beg < end) issue(sld(P.t.ent + beg) & 0x7fffffff, 0);
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[row][16ks + 8hh .. +8].
   bf16x8 qf[2][NKS];
@@ -74,27 +74,29 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
 
   for (int it = beg; it < end; ++it) {
     const int buf = (it - beg) & 1;
-    const uint32_t ent = (uint32_t)P.t.ent[it];
+    const uint32_t ent = (uint32_t)sld(P.t.ent + it);
     const int kt = (int)(ent & 0x7fffffffu);
     const bool partial = (ent & ENT_PARTIAL) != 0;
     wait_vmem();
     __syncthreads();
-    if (it + 1 < end) issue(P.t.ent[it + 1] & 0x7fffffff, buf ^ 1);
-    const bf16* Ks = smem + buf * (KT + VT);
-    const bf16* Vs = Ks + KT;
 
-    // Allowed-key masks of this lane's two rows (PARTIAL and ragged tiles only),
-    // evaluated before the scores are live.
+    // Allowed-key masks of this lane's two rows (PARTIAL and ragged tiles
+    // only), evaluated before the next tile's loads are issued so that the
+    // mask table reads never wait behind them.
     const bool masked = partial || (kt + 1) * BN > P.Tk;
     uint32_t mbits[2][2];
     if (masked) {
-      const int aux = partial ? P.t.ent_aux[it] : -1;
+      const int aux = partial ? sld(P.t.ent_aux + it) : -1;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
           mbits[b][kb] = keymask32(P.m, aux, mg, partial, row_base + b * 32 + li, kt * BN + kb * 32);
+      wait_vmem();
     }
+    if (it + 1 < end) issue(sld(P.t.ent + it + 1) & 0x7fffffff, buf ^ 1);
+    const bf16* Ks = smem + buf * (KT + VT);
+    const bf16* Vs = Ks + KT;
     __builtin_amdgcn_sched_barrier(0);
 
     // 1. S^T for 2 key blocks x 2 query blocks.

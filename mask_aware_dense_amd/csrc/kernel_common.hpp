@@ -127,15 +127,74 @@ constexpr int tile_rs() {
 template <int D, int KIND>
 constexpr int tile_elems() { return 64 * tile_rs<D, KIND>(); }
 
-// Direct global -> LDS copy of 16 bytes per lane (gfx950
+// Direct global -> LDS copies of 16 bytes per lane (gfx950
 // global_load_lds_dwordx4): lane l of the wave writes LDS bytes
-// [lds_base + 16 l, +16).  lds_base must be wave-uniform.
-__device__ __forceinline__ void g2lds16(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+// [lds + 16 l, +16); the LDS base goes in M0 and must be wave-uniform.
+//
+// They are issued from inline assembly on purpose.  The compiler treats a
+// direct LDS load it issued itself as a pending LDS write that may alias
+// every later LDS read, and so waits for all outstanding vector-memory
+// operations (vmcnt 0) before the first LDS read that follows -- which
+// turns a prefetch of the next tile into a serial load.  Here the kernels
+// own that ordering: they wait for a buffer's loads explicitly
+// (wait_vmem / wait_vmem_le) and then pass a workgroup barrier before any
+// wave reads it.  M0 is saved and restored around the copy.
+// The LDS address and the source base are wave-uniform by contract; the
+// readfirstlane only tells the compiler so (it folds away for values already
+// in scalar registers).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p));
 }
-// Wait until this wave's outstanding vector-memory loads (including direct
-// LDS loads) have completed.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t x = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+// Source = base (wave-uniform) + voff (per lane, bytes).
+__device__ __forceinline__ void g2lds16(const void* base, uint32_t voff, const void* lds) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(voff), "s"(uniform_ptr(base)), "s"(lds_addr(lds))
+      : "memory");
+}
+// Source = per-lane 64-bit address.
+__device__ __forceinline__ void g2lds16(const void* g, const void* lds) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(g), "s"(lds_addr(lds))
+      : "memory");
+}
+// Wait until this wave's outstanding vector-memory operations (including
+// direct LDS loads) have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until at most N of them are outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Scalar load of a wave-uniform read-only value (tile lists, plan tables):
+// through the constant address space the load goes to the scalar unit
+// instead of a vector load plus readfirstlane, and it does not share the
+// vector-memory counter with the direct LDS loads in flight.
+template <typename T>
+__device__ __forceinline__ T sld(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
 
 // Storage row p of a tile holds tensor row tile_row(p): p itself, or swap23
 // within 32-row blocks for tiles read as the score MFMA's A operand.
@@ -173,7 +232,7 @@ struct TileLoader {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int ii = i * NW + w;
-        if (ii < SPR) g2lds16(base + off[i], lds + ii * 512);
+        if (ii < SPR) g2lds16(base, off[i], lds + ii * 512);
       }
     } else {
 #pragma unroll
@@ -221,15 +280,17 @@ __device__ __forceinline__ uint32_t keymask32(const MaskDev& m, int32_t aux, int
   } else if (m.mode == MODE_SLICES) {
     bits = 0u;
     const int32_t* lst = m.tile_slices + aux;
-    const int n = lst[0];
+    const int n = sld(lst);
     for (int x = 0; x < n; ++x) {
-      const mad_slice s = m.slices[lst[1 + x]];
-      if (i < s.q0 || i >= s.q1) continue;
-      int lo = s.k0, hi = s.k1;
-      if (s.type == MAD_SLICE_CAUSAL) {
-        const int off = i - s.q0;
-        hi = min(hi, s.k0 + off + 1);
-        if (s.window > 0) lo = max(lo, s.k0 + off - s.window + 1);
+      const int32_t* sp = &m.slices[sld(lst + 1 + x)].q0;  // q0 q1 k0 k1 type window
+      const int q0 = sld(sp), q1 = sld(sp + 1), k0 = sld(sp + 2), k1 = sld(sp + 3);
+      const int type = sld(sp + 4), window = sld(sp + 5);
+      if (i < q0 || i >= q1) continue;
+      int lo = k0, hi = k1;
+      if (type == MAD_SLICE_CAUSAL) {
+        const int off = i - q0;
+        hi = min(hi, k0 + off + 1);
+        if (window > 0) lo = max(lo, k0 + off - window + 1);
       }
       bits |= range_bits(lo - key0, hi - key0);
     }
