@@ -136,6 +136,7 @@ extern "C" mad_status mad_plan_upload(mad_plan* p, hipStream_t stream) {
   const size_t off_rq = add(p->row_qb.data(), p->row_qb.size() * 4);
   const size_t off_ck = add(p->col_kb.data(), p->col_kb.size() * 4);
   const size_t off_ke = add(p->k_edges.data(), p->k_edges.size() * 4);
+  const size_t off_qe = add(p->q_edges.data(), p->q_edges.size() * 4);
   const size_t off_kp = add(p->keep.data(), p->keep.size() * 8);
   if (total == 0) total = 256;
   void* mem = nullptr;
@@ -174,6 +175,7 @@ extern "C" mad_status mad_plan_upload(mad_plan* p, hipStream_t stream) {
   m.row_qb = (const int32_t*)(base + off_rq);
   m.col_kb = (const int32_t*)(base + off_ck);
   m.k_edges = (const int32_t*)(base + off_ke);
+  m.q_edges = (const int32_t*)(base + off_qe);
   m.keep = (const uint64_t*)(base + off_kp);
   m.n_qb = p->n_qb;
   m.n_kb = p->n_kb;
@@ -223,7 +225,7 @@ extern "C" mad_status mad_bwd_workspace_bytes(const mad_plan* p, int32_t Tq, int
   if (!p) return fail(MAD_ERR_INVALID, "mad_bwd_workspace_bytes: plan is NULL");
   if (Tq < 0 || Tk < 0 || Hq <= 0 || Hkv <= 0) return fail(MAD_ERR_INVALID, "mad_bwd_workspace_bytes: bad sizes");
   if (d != 64 && d != 128) return fail(MAD_ERR_UNSUPPORTED, "mad_bwd_workspace_bytes: head dim must be 64 or 128");
-  // delta and lse2 rows, each [Hq][Tq rounded up to 128] fp32
+  // -delta and -LSE/scale rows, each [Hq][Tq rounded up to 128] fp32
   const size_t tq_pad = ((size_t)Tq + 127) / 128 * 128;
   *bytes = 2 * (size_t)Hq * tq_pad * 4;
   return MAD_OK;
@@ -255,8 +257,8 @@ extern "C" mad_status mad_attn_bwd_phases(const mad_plan* p, const void* q, cons
   Pq.d_o = (const bf16*)d_o;
   Pq.lse_in = lse;
   Pq.Tq_pad = (int32_t)(((int64_t)Tq + 127) / 128 * 128);
-  Pq.delta = (float*)workspace;
-  Pq.lse2 = (float*)workspace + (size_t)Hq * Pq.Tq_pad;
+  Pq.ndelta = (float*)workspace;
+  Pq.nlse = (float*)workspace + (size_t)Hq * Pq.Tq_pad;
   Pq.dq = (bf16*)dq;
   Pq.dk = (bf16*)dk;
   Pq.dv = (bf16*)dv;

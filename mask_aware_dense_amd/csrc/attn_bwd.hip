@@ -15,8 +15,11 @@
 // key-tile list (the forward's tiling).  Both recompute P from LSE.
 //
 // Workspace (fp32, rows padded to a multiple of 128 per head):
-//   delta[h][i] = D_i and lse2[h][i] = LSE_i log2(e), with lse2 = +inf for rows
-//   that have no allowed key or lie past Tq -- so their P is exactly 0.
+//   ndelta[h][i] = -D_i and nlse[h][i] = -LSE_i / scale, with nlse = -inf for
+//   rows that have no allowed key or lie past Tq -- so their P is exactly 0.
+// Both are stored negated so that the dK/dV kernel can start its score and
+// dP accumulators from them: P = exp2(scale log2e (q.k + nlse)) and
+// dS = P (dP + ndelta).
 #include "kernel_common.hpp"
 
 namespace mad {
@@ -43,13 +46,13 @@ __global__ __launch_bounds__(256) void delta_kernel(const AttnParams P) {
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
   if (r < nrows && sub == 0) {
-    float l2 = INFINITY;
+    float nl = -INFINITY;
     if (in) {
       const float l = P.lse_in[h * P.Tq + i];
-      l2 = (l == -INFINITY) ? INFINITY : l * LOG2E;
+      if (l != -INFINITY) nl = -l / P.scale;
     }
-    P.delta[h * P.Tq_pad + i] = acc;
-    P.lse2[h * P.Tq_pad + i] = l2;
+    P.ndelta[h * P.Tq_pad + i] = -acc;
+    P.nlse[h * P.Tq_pad + i] = nl;
   }
 }
 
@@ -59,7 +62,7 @@ __global__ __launch_bounds__(256) void delta_kernel(const AttnParams P) {
 // by direct loads into a double buffer (both stored with the swap23 row order).
 // Per key block of 32 keys:
 //   S^T = K Q^T, dP^T = V dO^T       (keys x queries; lane = query row)
-//   P^T = exp2(S^T scale log2e - lse2), dS^T = P^T (dP^T - D)
+//   P^T = exp2((S^T scale - LSE) log2e), dS^T = P^T (dP^T - D)
 //   dQ^T += K^T dS^T                 (K^T read transposed from LDS)
 // ---------------------------------------------------------------------------
 template <int D>
@@ -93,7 +96,7 @@ __global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
   if (beg < end) issue(sld(P.t.ent + beg) & 0x7fffffff, 0);
 
   bf16x8 qf[2][NKS], df[2][NKS];
-  float lse2[2], dlt[2];
+  float ml2[2], ndl[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int row = row_base + b * 32 + li;
@@ -105,8 +108,8 @@ __global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
       qf[b][ks] = ld16(qs + 16 * ks);
       df[b][ks] = ld16(ds + 16 * ks);
     }
-    lse2[b] = P.lse2[(int64_t)h * P.Tq_pad + row];
-    dlt[b] = P.delta[(int64_t)h * P.Tq_pad + row];
+    ml2[b] = P.nlse[(int64_t)h * P.Tq_pad + row] * P.scale_log2;  // -LSE log2(e)
+    ndl[b] = P.ndelta[(int64_t)h * P.Tq_pad + row];
   }
 
   f32x16 acc[NDB][2];
@@ -173,8 +176,8 @@ __global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], P.scale_log2, -lse2[b]));
-          s[b][r] = pv * (dp[b][r] - dlt[b]);
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], P.scale_log2, ml2[b]));
+          s[b][r] = pv * (dp[b][r] + ndl[b]);
         }
       // dQ^T += K^T dS^T: keys 16 t2 + 8 hh + 0..3 live in LDS rows 16 t2 + 4 hh + 0..3, keys +4..7 in rows +8.
 #pragma unroll
@@ -211,182 +214,7 @@ __global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// dK/dV kernel: one workgroup per (KV head, 128-key tile), four waves of 32
-// keys each.  K and V of the wave's keys stay in registers; for every query
-// head of the GQA group and every query tile (64 rows) in the key tile's
-// list, the Q / dO tiles and their lse2 / delta rows arrive by direct loads
-// into a double buffer, and
-//   S = Q K^T, dP = dO V^T           (queries x keys; lane = key)
-//   P = exp2(S scale log2e - lse2), dS = P (dP - D)
-//   dV += P^T dO, dK += dS^T Q       (dO and Q read transposed from LDS)
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
-  constexpr int BM = BM1, BN = BN1, NKS = D / 16, NDB = D / 32;
-  constexpr int TILE = tile_elems<D, TILE_MIXED>(), RS = tile_rs<D, TILE_MIXED>();
-  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];   // Q0 dO0 Q1 dO1
-  __shared__ __attribute__((aligned(256))) float rowv[2][2 * BM];  // per buffer: lse2[64], delta[64]
-  __shared__ uint32_t mask_s[BM * 4];
-
-  const int L = blockIdx.x;
-  const int kt = sld(P.t.order + L / P.Hkv);
-  const int g = L % P.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, li = lane & 31;
-  const int key = kt * BN + w * 32 + li;
-  const int kc = min(key, P.Tk - 1);
-
-  // K, V of this lane's key as B operands: lane holds K[key][16ks + 8hh .. +8].
-  bf16x8 kf[NKS], vf[NKS];
-  {
-    const bf16* ks_ = P.k + (int64_t)kc * P.k_tok + (int64_t)g * P.k_head + 8 * hh;
-    const bf16* vs_ = P.v + (int64_t)kc * P.v_tok + (int64_t)g * P.v_head + 8 * hh;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      kf[ks] = ld16(ks_ + 16 * ks);
-      vf[ks] = ld16(vs_ + 16 * ks);
-    }
-  }
-  f32x16 dka[NDB], dva[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    dka[db] = f32x16{};
-    dva[db] = f32x16{};
-  }
-
-  // Flattened walk over (query head of the group, query tile of that head's
-  // list), kept as two cursors: the item being computed and the next one,
-  // whose tiles are prefetched.
-  struct Cursor {
-    int e, it, end;
-  };
-  auto head_list = [&](int e, Cursor& c) {
-    const int32_t* ptr = P.t.ptr + (int64_t)((g * P.R + e) / P.grp_div) * (P.t.nmajor + 1);
-    c.e = e;
-    c.it = sld(ptr + kt);
-    c.end = sld(ptr + kt + 1);
-  };
-  auto settle = [&](Cursor& c) {  // move past exhausted heads
-    while (c.it >= c.end && c.e + 1 < P.R) head_list(c.e + 1, c);
-  };
-  TileLoader<D, TILE_MIXED, 4, false> qload, dload;
-  qload.init(P.q_tok, w, lane);
-  dload.init((int64_t)P.Hq * D, w, lane);
-  auto issue = [&](const Cursor& c, int buf) {
-    const int hx = g * P.R + c.e;
-    const int q0 = (sld(P.t.ent + c.it) & 0x7fffffff) * BM;
-    qload.issue(smem + (2 * buf) * TILE, P.q + (int64_t)hx * P.q_head, P.q_tok, q0, P.Tq, w, lane);
-    dload.issue(smem + (2 * buf + 1) * TILE, P.d_o + (int64_t)hx * D, (int64_t)P.Hq * D, q0, P.Tq, w, lane);
-    if (w == 0 && lane < 32) {
-      const float* src = (lane < 16 ? P.lse2 : P.delta) + (int64_t)hx * P.Tq_pad + q0 + 4 * (lane & 15);
-      g2lds16(src, &rowv[buf][0]);
-    }
-  };
-  Cursor cur;
-  head_list(0, cur);
-  settle(cur);
-  if (cur.it < cur.end) issue(cur, 0);
-
-  for (int n = 0; cur.it < cur.end; ++n) {
-    const int buf = n & 1;
-    const int h = g * P.R + cur.e;
-    const int it = cur.it;
-    const int mg = h / P.grp_div;
-    const uint32_t ent = (uint32_t)sld(P.t.ent + it);
-    const int qt = (int)(ent & 0x7fffffffu);
-    const bool partial = (ent & ENT_PARTIAL) != 0;
-    const int q0 = qt * BM;
-    Cursor nxt = cur;
-    ++nxt.it;
-    settle(nxt);
-    wait_vmem();
-    __syncthreads();
-    // Mask words of a PARTIAL tile are built before the next tiles' loads
-    // are issued, so that the mask table reads never wait behind them.
-    if (partial) {
-      mask_s[tid] = keymask32(P.m, sld(P.t.ent_aux + it), mg, true, q0 + (tid >> 2), kt * BN + 32 * (tid & 3));
-      wait_vmem();
-    }
-    if (nxt.it < nxt.end) issue(nxt, buf ^ 1);
-    if (partial) __syncthreads();
-    const bf16* Qs = smem + (2 * buf) * TILE;
-    const bf16* Ds = smem + (2 * buf + 1) * TILE;
-    const float* lse_s = &rowv[buf][0];
-    const float* dlt_s = &rowv[buf][BM];
-
-    // S, dP for 2 query blocks of 32 rows x this wave's 32 keys.
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      s[b] = f32x16{};
-      dp[b] = f32x16{};
-    }
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int off = (b * 32 + li) * RS + (16 * ks + 8 * hh);
-        const bf16x8 aq = ld16(Qs + off);
-        const bf16x8 ad = ld16(Ds + off);
-        s[b] = mfma32(aq, kf[ks], s[b]);
-        dp[b] = mfma32(ad, vf[ks], dp[b]);
-      }
-
-    // P and dS; register r of block b holds query row b*32 + 8(r/4) + 4hh + r%4.
-    f32x16 ds[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int rr = b * 32 + 8 * rg + 4 * hh;
-        const float4 l4 = *reinterpret_cast<const float4*>(lse_s + rr);
-        const float4 d4 = *reinterpret_cast<const float4*>(dlt_s + rr);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv_[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int r = 4 * rg + x;
-          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], P.scale_log2, -lv[x]));
-          if (partial && !((mask_s[(rr + x) * 4 + w] >> li) & 1u)) pv = 0.f;
-          s[b][r] = pv;
-          ds[b][r] = pv * (dp[b][r] - dv_[x]);
-        }
-      }
-
-    // dV += P^T dO and dK += dS^T Q over the 64 query rows (4 k-steps of 16).
-    // Contraction element e of lane half hh in k-step (b, t2) is query row
-    // b*32 + 16 t2 + 8(e/4) + 4hh + e%4 -- registers 8 t2 .. 8 t2 + 7.
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const bf16x8 pa = to_bf16x8(s[b], 8 * t2);
-        const bf16x8 sa = to_bf16x8(ds[b], 8 * t2);
-        const int qrow = b * 32 + 16 * t2 + 4 * hh + tr_row(lane);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int col = db * 32 + tr_col(lane);
-          const bf16x8 bd = ld_tr8(Ds + (qrow) * RS + (col), Ds + (qrow + 8) * RS + (col));
-          const bf16x8 bq = ld_tr8(Qs + (qrow) * RS + (col), Qs + (qrow + 8) * RS + (col));
-          dva[db] = mfma32(pa, bd, dva[db]);
-          dka[db] = mfma32(sa, bq, dka[db]);
-        }
-      }
-    cur = nxt;
-  }
-
-  // dK, dV: lane holds column d = db*32 + li of key rows 8(r/4) + 4hh + r%4 of the wave's 32 keys.
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kk = kt * BN + w * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (kk < P.Tk) {
-        const int64_t off = ((int64_t)kk * P.Hkv + g) * D + db * 32 + li;
-        P.dk[off] = (bf16)(dka[db][r] * P.scale);
-        P.dv[off] = (bf16)dva[db][r];
-      }
-    }
-}
+hipError_t launch_dkdv(const AttnParams& P, int D, int n_items, hipStream_t stream);
 
 hipError_t launch_bwd(const AttnParams& Pq, const AttnParams& Pkv, int D, int nq_items, int nkv_items,
                       uint32_t phases, hipStream_t stream) {
@@ -400,11 +228,9 @@ hipError_t launch_bwd(const AttnParams& Pq, const AttnParams& Pkv, int D, int nq
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if ((phases & MAD_BWD_DKDV) && nkv_items > 0) {
-    if (D == 128) hipLaunchKernelGGL(dkdv_kernel<128>, dim3(nkv_items), dim3(256), 0, stream, Pkv);
-    else hipLaunchKernelGGL(dkdv_kernel<64>, dim3(nkv_items), dim3(256), 0, stream, Pkv);
+    err = launch_dkdv(Pkv, D, nkv_items, stream);
+    if (err != hipSuccess) return err;
   }
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
   if ((phases & MAD_BWD_DQ) && nq_items > 0) {
     if (D == 128) hipLaunchKernelGGL(dq_kernel<128>, dim3(nq_items), dim3(128), 0, stream, Pq);
     else hipLaunchKernelGGL(dq_kernel<64>, dim3(nq_items), dim3(128), 0, stream, Pq);

@@ -1,0 +1,242 @@
+// attn_dkdv.hip -- dK / dV kernel for gfx950.
+//
+// For every key j of a KV head and every query head h of its GQA group
+// (LongCA-bench section 3.2 names the backward pass as the bottleneck):
+//   P_ij  = exp(scale q_i.k_j - LSE_i)          (0 where (i, j) is masked)
+//   dS_ij = P_ij (dO_i.v_j - D_i)
+//   dV_j  = sum_h sum_i P_ij dO_i,   dK_j = scale sum_h sum_i dS_ij q_i
+//
+// Work decomposition: one workgroup per (KV head, 128-key tile), four waves
+// of 32 keys.  K and V of the wave's keys stay in registers as MFMA operands.
+// The workgroup walks, for each query head of the group, the key tile's list
+// of non-EMPTY 64-row query tiles; the Q / dO tiles and their -LSE/scale and
+// -D rows come in by direct global->LDS loads into a double buffer.
+//
+// One item (64 query rows x the wave's 32 keys) runs in four stages, as two
+// 32-row blocks b0 / b1, arranged so that the matrix cores always have work
+// while the vector unit computes P and dS:
+//   A  S0 = Q0 K^T, dP0 = dO0 V^T       (MFMA)
+//   B  S1, dP1 (MFMA)        +  P0, dS0 (VALU)
+//   C  dV += P0^T dO0, dK += dS0^T Q0 (MFMA)  +  P1, dS1 (VALU)
+//   D  dV += P1^T dO1, dK += dS1^T Q1 (MFMA)
+// The score and dP accumulators start from -LSE/scale and -D (read from LDS
+// straight into the accumulator registers), so S holds q.k - LSE/scale and
+// dP holds dO.v - D when the products finish.  LDS operands are read two
+// MFMA steps ahead of their use through a three-slot register ring; every
+// step ends in a scheduling fence so that the compiler keeps that distance.
+#include "kernel_common.hpp"
+
+namespace mad {
+
+template <int D>
+__global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
+  constexpr int BM = BM1, BN = BN1, NKS = D / 16, NDB = D / 32;
+  constexpr int TILE = tile_elems<D, TILE_MIXED>(), RS = tile_rs<D, TILE_MIXED>();
+  constexpr int S1 = 2 * NKS;   // phase-1 steps (block, k-step)
+  constexpr int S2 = 4 * NDB;   // phase-2 steps (block, t2, d-block)
+  constexpr int EB = 16 / NKS;  // P / dS elements per stage-B step
+  constexpr int EC = 16 / (2 * NDB);  // P / dS elements per stage-C step
+  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];   // Q0 dO0 Q1 dO1
+  __shared__ __attribute__((aligned(256))) float rowv[2][2 * BM];  // per buffer: -LSE/scale[64], -D[64]
+
+  const int L = blockIdx.x;
+  const int kt = sld(P.t.order + L / P.Hkv);
+  const int g = L % P.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, li = lane & 31;
+  const int key = kt * BN + w * 32 + li;
+  const int kc = min(key, P.Tk - 1);
+  const float c = P.scale_log2;
+
+  // K, V of this lane's key as B operands: lane holds K[key][16ks + 8hh .. +8].
+  bf16x8 kf[NKS], vf[NKS];
+  {
+    const bf16* ks_ = P.k + (int64_t)kc * P.k_tok + (int64_t)g * P.k_head + 8 * hh;
+    const bf16* vs_ = P.v + (int64_t)kc * P.v_tok + (int64_t)g * P.v_head + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      kf[ks] = ld16(ks_ + 16 * ks);
+      vf[ks] = ld16(vs_ + 16 * ks);
+    }
+  }
+  f32x16 dka[NDB], dva[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dka[db] = f32x16{};
+    dva[db] = f32x16{};
+  }
+
+  // Flattened walk over (query head of the group, query tile of that head's
+  // list), kept as two cursors: the item being computed and the next one,
+  // whose tiles are prefetched.
+  struct Cursor {
+    int e, it, end;
+  };
+  auto head_list = [&](int e, Cursor& cu) {
+    const int32_t* ptr = P.t.ptr + (int64_t)((g * P.R + e) / P.grp_div) * (P.t.nmajor + 1);
+    cu.e = e;
+    cu.it = sld(ptr + kt);
+    cu.end = sld(ptr + kt + 1);
+  };
+  auto settle = [&](Cursor& cu) {  // move past exhausted heads
+    while (cu.it >= cu.end && cu.e + 1 < P.R) head_list(cu.e + 1, cu);
+  };
+  TileLoader<D, TILE_MIXED, 4, false> qload, dload;
+  qload.init(P.q_tok, w, lane);
+  dload.init((int64_t)P.Hq * D, w, lane);
+  auto issue = [&](const Cursor& cu, int buf) {
+    const int hx = g * P.R + cu.e;
+    const int q0 = (sld(P.t.ent + cu.it) & 0x7fffffff) * BM;
+    qload.issue(smem + (2 * buf) * TILE, P.q + (int64_t)hx * P.q_head, P.q_tok, q0, P.Tq, w, lane);
+    dload.issue(smem + (2 * buf + 1) * TILE, P.d_o + (int64_t)hx * D, (int64_t)P.Hq * D, q0, P.Tq, w, lane);
+    if (w == 0 && lane < 32) {
+      const float* src = (lane < 16 ? P.nlse : P.ndelta) + (int64_t)hx * P.Tq_pad + q0 + 4 * (lane & 15);
+      g2lds16(src, &rowv[buf][0]);
+    }
+  };
+  // The K / V register loads complete before the first tiles are requested:
+  // the loop's waits count the direct loads, which the compiler does not track.
+  wait_vmem();
+  Cursor cur;
+  head_list(0, cur);
+  settle(cur);
+  if (cur.it < cur.end) issue(cur, 0);
+
+  for (int n = 0; cur.it < cur.end; ++n) {
+    const int buf = n & 1;
+    const int h = g * P.R + cur.e;
+    const int mg = h / P.grp_div;
+    const uint32_t ent = (uint32_t)sld(P.t.ent + cur.it);
+    const bool partial = (ent & ENT_PARTIAL) != 0;
+    const int q0 = (int)(ent & 0x7fffffffu) * BM;
+    Cursor nxt = cur;
+    ++nxt.it;
+    settle(nxt);
+    wait_vmem();
+    __syncthreads();
+    // Rows of the tile this lane's key may see (PARTIAL tiles), evaluated
+    // before the next tiles' loads are issued so that the mask table reads
+    // never wait behind them.
+    uint32_t mw[2] = {0u, 0u};
+    if (partial) {
+      const uint64_t rows = rowmask64(P.m, sld(P.t.ent_aux + cur.it), mg, key, q0);
+      mw[0] = (uint32_t)(rows >> (4 * hh));
+      mw[1] = (uint32_t)(rows >> (32 + 4 * hh));
+      wait_vmem();
+    }
+    if (nxt.it < nxt.end) issue(nxt, buf ^ 1);
+    const bf16* Qs = smem + (2 * buf) * TILE;
+    const bf16* Ds = smem + (2 * buf + 1) * TILE;
+    const float* nl_s = &rowv[buf][0];
+    const float* nd_s = &rowv[buf][BM];
+
+    {
+      // Register r of block b holds query row b*32 + 8(r/4) + 4hh + r%4.  A
+      // masked row starts its score at -inf, so its P (and dS) is exactly 0
+      // after the products: the mask costs nothing past the initialisation.
+      f32x16 sc[2], dp[2];
+      auto init = [&](int b) {
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int rr = b * 32 + 8 * rg + 4 * hh;
+          const float4 l4 = *reinterpret_cast<const float4*>(nl_s + rr);
+          const float4 d4 = *reinterpret_cast<const float4*>(nd_s + rr);
+          sc[b][4 * rg + 0] = l4.x; sc[b][4 * rg + 1] = l4.y; sc[b][4 * rg + 2] = l4.z; sc[b][4 * rg + 3] = l4.w;
+          dp[b][4 * rg + 0] = d4.x; dp[b][4 * rg + 1] = d4.y; dp[b][4 * rg + 2] = d4.z; dp[b][4 * rg + 3] = d4.w;
+        }
+        if (partial) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (!((mw[b] >> (8 * (r >> 2) + (r & 3))) & 1u)) sc[b][r] = -INFINITY;
+        }
+      };
+      // Phase-1 operands of step st: Q and dO rows b*32 + li, columns 16ks + 8hh.
+      bf16x8 opq[3], opd[3];
+      auto ld1 = [&](int st) {
+        const int b = st / NKS, ks = st % NKS, off = (b * 32 + li) * RS + 16 * ks + 8 * hh;
+        opq[st % 3] = ld16(Qs + off);
+        opd[st % 3] = ld16(Ds + off);
+      };
+      // Phase-2 operands of step st: dO and Q read transposed; contraction
+      // element e of half-wave hh is query row b*32 + 16 t2 + 8(e/4) + 4hh + e%4.
+      bf16x8 trd[3], trq[3];
+      auto ld2 = [&](int st) {
+        const int b = st / (2 * NDB), t2 = (st / NDB) % 2, db = st % NDB;
+        const int qrow = b * 32 + 16 * t2 + 4 * hh + tr_row(lane), col = db * 32 + tr_col(lane);
+        trd[st % 3] = ld_tr8(Ds + qrow * RS + col, Ds + (qrow + 8) * RS + col);
+        trq[st % 3] = ld_tr8(Qs + qrow * RS + col, Qs + (qrow + 8) * RS + col);
+      };
+      // P = exp2(c S) and dS = P dP for registers r, r + 1 of block b,
+      // written as bf16 straight into the phase-2 A operands: register r
+      // feeds element r % 8 of k-step t2 = r / 8.
+      bf16x8 pa[2][2], sa[2][2];  // [block][t2]
+      auto pds = [&](int b, int r) {
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const float pv = __builtin_amdgcn_exp2f(sc[b][r + x] * c);
+          pa[b][(r + x) >> 3][(r + x) & 7] = (bf16)pv;
+          sa[b][(r + x) >> 3][(r + x) & 7] = (bf16)(pv * dp[b][r + x]);
+        }
+      };
+
+      init(0);
+      ld1(0);
+      ld1(1);
+      init(1);
+      __builtin_amdgcn_sched_barrier(0);
+      // Stage A.
+#pragma unroll
+      for (int st = 0; st < NKS; ++st) {
+        ld1(st + 2);
+        sc[0] = mfma32(opq[st % 3], kf[st], sc[0]);
+        dp[0] = mfma32(opd[st % 3], vf[st], dp[0]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // Stage B.
+#pragma unroll
+      for (int st = NKS; st < S1; ++st) {
+        if (st + 2 < S1) ld1(st + 2);
+        else ld2(st + 2 - S1);
+        sc[1] = mfma32(opq[st % 3], kf[st - NKS], sc[1]);
+        dp[1] = mfma32(opd[st % 3], vf[st - NKS], dp[1]);
+#pragma unroll
+        for (int x = 0; x < EB; x += 2) pds(0, (st - NKS) * EB + x);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // Stages C and D.
+#pragma unroll
+      for (int st = 0; st < S2; ++st) {
+        if (st + 2 < S2) ld2(st + 2);
+        const int b = st / (2 * NDB), t2 = (st / NDB) % 2, db = st % NDB;
+        dva[db] = mfma32(pa[b][t2], trd[st % 3], dva[db]);
+        dka[db] = mfma32(sa[b][t2], trq[st % 3], dka[db]);
+        if (st < 2 * NDB) {
+#pragma unroll
+          for (int x = 0; x < EC; x += 2) pds(1, st * EC + x);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    cur = nxt;
+  }
+
+  // dK, dV: lane holds column d = db*32 + li of key rows 8(r/4) + 4hh + r%4 of the wave's 32 keys.
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kk = kt * BN + w * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      if (kk < P.Tk) {
+        const int64_t off = ((int64_t)kk * P.Hkv + g) * D + db * 32 + li;
+        P.dk[off] = (bf16)(dka[db][r] * P.scale);
+        P.dv[off] = (bf16)dva[db][r];
+      }
+    }
+}
+
+hipError_t launch_dkdv(const AttnParams& P, int D, int n_items, hipStream_t stream) {
+  if (D == 128) hipLaunchKernelGGL(dkdv_kernel<128>, dim3(n_items), dim3(256), 0, stream, P);
+  else hipLaunchKernelGGL(dkdv_kernel<64>, dim3(n_items), dim3(256), 0, stream, P);
+  return hipGetLastError();
+}
+
+}  // namespace mad

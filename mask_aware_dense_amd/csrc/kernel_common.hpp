@@ -39,8 +39,8 @@ struct AttnParams {
   const bf16* o_in;   // backward: forward output
   const bf16* d_o;    // backward: upstream gradient (packed [Tq, Hq, D])
   const float* lse_in;
-  float* delta;       // backward: rowsum(dO * O), [Hq, Tq_pad]
-  float* lse2;        // backward: LSE * log2(e), +inf for empty / padded rows, [Hq, Tq_pad]
+  float* ndelta;      // backward: -rowsum(dO * O), [Hq, Tq_pad]
+  float* nlse;        // backward: -LSE / scale, -inf for empty / padded rows, [Hq, Tq_pad]
   int32_t Tq_pad;     // Tq rounded up to a multiple of 128
   bf16* dq;
   bf16* dk;
@@ -308,6 +308,55 @@ __device__ __forceinline__ uint32_t keymask32(const MaskDev& m, int32_t aux, int
   const int nvalid = m.Tk - key0;
   if (nvalid < 32) bits &= (nvalid <= 0) ? 0u : ((1u << nvalid) - 1u);
   if (i >= m.Tq) bits = 0u;
+  return bits;
+}
+
+__device__ __forceinline__ uint64_t range_bits64(int a, int b) {
+  a = max(a, 0);
+  b = min(b, 64);
+  if (a >= b) return 0ull;
+  const uint64_t hi = (b == 64) ? ~0ull : ((1ull << b) - 1ull);
+  return hi & ~((1ull << a) - 1ull);
+}
+
+// Allowed query rows among [row0, row0 + 64) for key j of a visited PARTIAL
+// tile of the dK/dV tiling, as a bitmask (bit r <-> row row0 + r): the same
+// predicate as keymask32, read along the key's column.  Rows >= Tq and keys
+// >= Tk are never allowed.
+__device__ __forceinline__ uint64_t rowmask64(const MaskDev& m, int32_t aux, int32_t grp, int j, int row0) {
+  uint64_t bits = 0ull;
+  if (j < m.Tk) {
+    if (m.mode == MODE_SLICES) {
+      const int32_t* lst = m.tile_slices + aux;
+      const int n = sld(lst);
+      for (int x = 0; x < n; ++x) {
+        const int32_t* sp = &m.slices[sld(lst + 1 + x)].q0;  // q0 q1 k0 k1 type window
+        const int q0 = sld(sp), q1 = sld(sp + 1), k0 = sld(sp + 2), k1 = sld(sp + 3);
+        const int type = sld(sp + 4), window = sld(sp + 5);
+        if (j < k0 || j >= k1) continue;
+        int lo = q0, hi = q1;
+        if (type == MAD_SLICE_CAUSAL) {
+          const int off = j - k0;  // row i is allowed from i - q0 = off on ...
+          lo = max(lo, q0 + off);
+          if (window > 0) hi = min(hi, q0 + off + window);  // ... until i - q0 - off reaches the window
+        }
+        bits |= range_bits64(lo - row0, hi - row0);
+      }
+    } else {
+      const int rlast = min(row0 + 63, m.Tq - 1);
+      if (row0 <= rlast) {
+        const int qa = sld(m.row_qb + row0), qz = sld(m.row_qb + rlast);
+        const int kb = m.col_kb[j];
+        for (int qb = qa; qb <= qz; ++qb) {
+          const uint64_t* row = m.keep + ((size_t)grp * m.n_qb + qb) * m.nw;
+          if ((row[kb >> 6] >> (kb & 63)) & 1ull)
+            bits |= range_bits64(sld(m.q_edges + qb) - row0, sld(m.q_edges + qb + 1) - row0);
+        }
+      }
+    }
+  }
+  const int nvalid = m.Tq - row0;
+  if (nvalid < 64) bits &= (nvalid <= 0) ? 0ull : ((1ull << nvalid) - 1ull);
   return bits;
 }
 

@@ -75,6 +75,7 @@ struct MaskDev {
   const int32_t* row_qb;       // [Tq] query block of each row
   const int32_t* col_kb;       // [Tk] key block of each key
   const int32_t* k_edges;      // [n_kb + 1]
+  const int32_t* q_edges;      // [n_qb + 1]
   const uint64_t* keep;        // [G][n_qb][nw]
   int32_t n_qb, n_kb, nw;
 };
