@@ -57,19 +57,30 @@ __global__ __launch_bounds__(256) void delta_kernel(const AttnParams P) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ kernel: one workgroup per (query head, 128-row query tile), two waves of
-// 64 rows, walking the forward tiling's key-tile list.  K and V tiles come in
-// by direct loads into a double buffer (both stored with the swap23 row order).
-// Per key block of 32 keys:
+// dQ kernel: one workgroup per (query head, 128-row query tile), four waves
+// of 32 rows, walking the forward tiling's key-tile list.  K and V tiles come
+// in by direct loads into a double buffer (both stored with the swap23 row
+// order).  Per key block kb of 32 keys:
 //   S^T = K Q^T, dP^T = V dO^T       (keys x queries; lane = query row)
 //   P^T = exp2((S^T scale - LSE) log2e), dS^T = P^T (dP^T - D)
 //   dQ^T += K^T dS^T                 (K^T read transposed from LDS)
+// A 64-key tile runs in four stages so that the vector work of one key block
+// sits under the other block's matrix products:
+//   A  S, dP (kb 0)        B  S, dP (kb 1)  +  P, dS (kb 0)
+//   C  dQ (kb 0) + P, dS (kb 1)             D  dQ (kb 1)
+// LDS operands are read two MFMA steps ahead through three-slot register
+// rings, each step closed by a scheduling fence.  Masked scores start at
+// -inf, so their P is exactly 0 with no per-element test after the products.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
+__global__ __launch_bounds__(256) void dq_kernel(const AttnParams P) {
   constexpr int BM = BM0, BN = BN0, NKS = D / 16, NDB = D / 32;
   constexpr int KRS = tile_rs<D, TILE_MIXED>(), KT = tile_elems<D, TILE_MIXED>();
   constexpr int VRS = tile_rs<D, TILE_ROWS>(), VT = tile_elems<D, TILE_ROWS>();
+  constexpr int S1 = 2 * NKS;        // phase-1 steps (kb, k-step)
+  constexpr int S2 = 4 * NDB;        // phase-2 steps (kb, t2, d-block)
+  constexpr int EB = 16 / NKS;       // P / dS elements per stage-B step
+  constexpr int EC = 16 / (2 * NDB); // P / dS elements per stage-C step
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * (KT + VT)];  // K0 V0 K1 V1
 
   const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -78,45 +89,49 @@ __global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
   const int h = g * P.R + e;
   const int qt = sld(P.t.order + rank);
   const int mg = h / P.grp_div;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, li = lane & 31;
-  const int row_base = qt * BM + w * 64;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, li = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, wave-uniform
+  const int row = qt * BM + w * 32 + li;  // this lane's query row
+  const float c = P.scale_log2;
 
   const int32_t* ptr = P.t.ptr + (int64_t)mg * (P.t.nmajor + 1);
   const int beg = sld(ptr + qt), end = sld(ptr + qt + 1);
   const bf16* kg = P.k + (int64_t)g * P.k_head;
   const bf16* vg = P.v + (int64_t)g * P.v_head;
-  TileLoader<D, TILE_MIXED, 2, true> kload;
-  TileLoader<D, TILE_ROWS, 2, true> vload;
+  const uint32_t smem_lds = lds_addr(smem);
+  TileLoader<D, TILE_MIXED, 4, true> kload;
+  TileLoader<D, TILE_ROWS, 4, true> vload;
   kload.init(P.k_tok, w, lane);
   vload.init(P.v_tok, w, lane);
   auto issue = [&](int kt, int buf) {
-    kload.issue(smem + buf * (KT + VT), kg, P.k_tok, kt * BN, P.Tk, w, lane);
-    vload.issue(smem + buf * (KT + VT) + KT, vg, P.v_tok, kt * BN, P.Tk, w, lane);
+    const uint32_t kl = smem_lds + buf * (KT + VT) * 2;
+    kload.issue(kl, kg, P.k_tok, kt * BN, P.Tk, w, lane);
+    vload.issue(kl + KT * 2, vg, P.v_tok, kt * BN, P.Tk, w, lane);
   };
-  if (beg < end) issue(sld(P.t.ent + beg) & 0x7fffffff, 0);
 
-  bf16x8 qf[2][NKS], df[2][NKS];
-  float ml2[2], ndl[2];
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int row = row_base + b * 32 + li;
+  // Q and dO of this lane's row as B operands: lane holds Q[row][16ks + 8hh .. +8].
+  bf16x8 qf[NKS], df[NKS];
+  float ml2, ndl;
+  {
     const int rc = min(row, P.Tq - 1);
     const bf16* qs = P.q + (int64_t)rc * P.q_tok + (int64_t)h * P.q_head + 8 * hh;
     const bf16* ds = P.d_o + ((int64_t)rc * P.Hq + h) * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      qf[b][ks] = ld16(qs + 16 * ks);
-      df[b][ks] = ld16(ds + 16 * ks);
+      qf[ks] = ld16(qs + 16 * ks);
+      df[ks] = ld16(ds + 16 * ks);
     }
-    ml2[b] = P.nlse[(int64_t)h * P.Tq_pad + row] * P.scale_log2;  // -LSE log2(e)
-    ndl[b] = P.ndelta[(int64_t)h * P.Tq_pad + row];
+    ml2 = P.nlse[(int64_t)h * P.Tq_pad + row] * c;  // -LSE log2(e); -inf past Tq
+    ndl = P.ndelta[(int64_t)h * P.Tq_pad + row];
   }
+  // The register loads complete before the first tiles are requested: the
+  // loop's waits count the direct loads, which the compiler does not track.
+  wait_vmem();
+  if (beg < end) issue(sld(P.t.ent + beg) & 0x7fffffff, 0);
 
-  f32x16 acc[NDB][2];
+  f32x16 acc[NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[db][b] = f32x16{};
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
   for (int it = beg; it < end; ++it) {
     const int buf = (it - beg) & 1;
@@ -128,79 +143,92 @@ __global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
     __syncthreads();
     // Allowed-key masks (PARTIAL and ragged tiles), evaluated before the next
     // tile's loads are issued so that the mask table reads never wait behind them.
-    uint32_t mbits[2][2];
+    uint32_t mbits[2] = {0xffffffffu, 0xffffffffu};
     if (masked) {
       const int aux = partial ? sld(P.t.ent_aux + it) : -1;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-          mbits[kb][b] = keymask32(P.m, aux, mg, partial, row_base + b * 32 + li, kt * BN + kb * 32);
+      for (int kb = 0; kb < 2; ++kb) mbits[kb] = keymask32(P.m, aux, mg, partial, row, kt * BN + kb * 32);
       wait_vmem();
     }
     if (it + 1 < end) issue(sld(P.t.ent + it + 1) & 0x7fffffff, buf ^ 1);
     const bf16* Ks = smem + buf * (KT + VT);
     const bf16* Vs = Ks + KT;
 
+    // Register r of key block kb holds key kb*32 + 16(r/8) + 8hh + r%8.
+    f32x16 sc[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s[2], dp[2];
+      sc[kb] = f32x16{};
+      dp[kb] = f32x16{};
+    }
+    if (masked) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        s[b] = f32x16{};
-        dp[b] = f32x16{};
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!((mbits[kb] >> (16 * (r >> 3) + 8 * hh + (r & 7))) & 1u)) sc[kb][r] = -INFINITY;
+    }
+    bf16x8 opk[3], opv[3];
+    auto ld1 = [&](int st) {
+      const int kb = st / NKS, ks = st % NKS;
+      opk[st % 3] = ld16(Ks + (kb * 32 + li) * KRS + 16 * ks + 8 * hh);
+      opv[st % 3] = ld16(Vs + (kb * 32 + li) * VRS + 16 * ks + 8 * hh);
+    };
+    // dQ^T step (kb, t2, db): keys 16 t2 + 8 hh + 0..3 of block kb live in LDS
+    // rows 16 t2 + 4 hh + 0..3, keys +4..7 in rows +8.
+    bf16x8 trk[3];
+    auto ld2 = [&](int st) {
+      const int kb = st / (2 * NDB), t2 = (st / NDB) % 2, db = st % NDB;
+      const int krow = kb * 32 + 16 * t2 + 4 * hh + tr_row(lane), kcol = db * 32 + tr_col(lane);
+      trk[st % 3] = ld_tr8(Ks + krow * KRS + kcol, Ks + (krow + 8) * KRS + kcol);
+    };
+    bf16x8 sb[2][2];  // dS^T as B operands, [kb][t2]
+    auto pds = [&](int kb, int r) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r + x], c, ml2));
+        sb[kb][(r + x) >> 3][(r + x) & 7] = (bf16)(pv * (dp[kb][r + x] + ndl));
       }
+    };
+
+    ld1(0);
+    ld1(1);
+    __builtin_amdgcn_sched_barrier(0);
+    // Stage A.
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 ak = ld16(Ks + (kb * 32 + li) * KRS + 16 * ks + 8 * hh);
-        const bf16x8 av = ld16(Vs + (kb * 32 + li) * VRS + 16 * ks + 8 * hh);
+    for (int st = 0; st < NKS; ++st) {
+      ld1(st + 2);
+      sc[0] = mfma32(opk[st % 3], qf[st], sc[0]);
+      dp[0] = mfma32(opv[st % 3], df[st], dp[0]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Stage B.
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          s[b] = mfma32(ak, qf[b][ks], s[b]);
-          dp[b] = mfma32(av, df[b][ks], dp[b]);
-        }
+    for (int st = NKS; st < S1; ++st) {
+      if (st + 2 < S1) ld1(st + 2);
+      else ld2(st + 2 - S1);
+      sc[1] = mfma32(opk[st % 3], qf[st - NKS], sc[1]);
+      dp[1] = mfma32(opv[st % 3], df[st - NKS], dp[1]);
+#pragma unroll
+      for (int x = 0; x < EB; x += 2) pds(0, (st - NKS) * EB + x);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Stages C and D.
+#pragma unroll
+    for (int st = 0; st < S2; ++st) {
+      if (st + 2 < S2) ld2(st + 2);
+      const int kb = st / (2 * NDB), t2 = (st / NDB) % 2, db = st % NDB;
+      acc[db] = mfma32(trk[st % 3], sb[kb][t2], acc[db]);
+      if (st < 2 * NDB) {
+#pragma unroll
+        for (int x = 0; x < EC; x += 2) pds(1, st * EC + x);
       }
-      if (masked) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const uint32_t bits = mbits[kb][b];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = 16 * (r >> 3) + 8 * hh + (r & 7);
-            if (!((bits >> off) & 1u)) s[b][r] = -INFINITY;
-          }
-        }
-      }
-      // dS^T = P^T (dP^T - D), in s[].
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], P.scale_log2, ml2[b]));
-          s[b][r] = pv * (dp[b][r] + ndl[b]);
-        }
-      // dQ^T += K^T dS^T: keys 16 t2 + 8 hh + 0..3 live in LDS rows 16 t2 + 4 hh + 0..3, keys +4..7 in rows +8.
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        bf16x8 sb[2];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) sb[b] = to_bf16x8(s[b], 8 * t2);
-        const int krow = kb * 32 + 16 * t2 + 4 * hh + tr_row(lane);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int kcol = db * 32 + tr_col(lane);
-          const bf16x8 a = ld_tr8(Ks + krow * KRS + kcol, Ks + (krow + 8) * KRS + kcol);
-#pragma unroll
-          for (int b = 0; b < 2; ++b) acc[db][b] = mfma32(a, sb[b], acc[db][b]);
-        }
-      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int row = row_base + b * 32 + li;
-    if (row >= P.Tq) continue;
+  // dQ^T: lane holds query row `row`, column d = db*32 + 8(r/4) + 4hh + r%4.
+  if (row < P.Tq) {
     bf16* dst = P.dq + ((int64_t)row * P.Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -208,7 +236,7 @@ __global__ __launch_bounds__(128) void dq_kernel(const AttnParams P) {
       for (int rg = 0; rg < 4; ++rg) {
         bf16x4 v4;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) v4[x] = (bf16)(acc[db][b][4 * rg + x] * P.scale);
+        for (int x = 0; x < 4; ++x) v4[x] = (bf16)(acc[db][4 * rg + x] * P.scale);
         *reinterpret_cast<bf16x4*>(dst + db * 32 + 8 * rg + 4 * hh) = v4;
       }
   }
@@ -232,8 +260,8 @@ hipError_t launch_bwd(const AttnParams& Pq, const AttnParams& Pkv, int D, int nq
     if (err != hipSuccess) return err;
   }
   if ((phases & MAD_BWD_DQ) && nq_items > 0) {
-    if (D == 128) hipLaunchKernelGGL(dq_kernel<128>, dim3(nq_items), dim3(128), 0, stream, Pq);
-    else hipLaunchKernelGGL(dq_kernel<64>, dim3(nq_items), dim3(128), 0, stream, Pq);
+    if (D == 128) hipLaunchKernelGGL(dq_kernel<128>, dim3(nq_items), dim3(256), 0, stream, Pq);
+    else hipLaunchKernelGGL(dq_kernel<64>, dim3(nq_items), dim3(256), 0, stream, Pq);
   }
   return hipGetLastError();
 }

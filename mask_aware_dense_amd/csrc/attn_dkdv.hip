@@ -42,7 +42,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
   const int L = blockIdx.x;
   const int kt = sld(P.t.order + L / P.Hkv);
   const int g = L % P.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, li = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, li = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, wave-uniform
   const int key = kt * BN + w * 32 + li;
   const int kc = min(key, P.Tk - 1);
   const float c = P.scale_log2;
@@ -80,17 +81,19 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
   auto settle = [&](Cursor& cu) {  // move past exhausted heads
     while (cu.it >= cu.end && cu.e + 1 < P.R) head_list(cu.e + 1, cu);
   };
+  const uint32_t smem_lds = lds_addr(smem), rowv_lds = lds_addr(&rowv[0][0]);
   TileLoader<D, TILE_MIXED, 4, false> qload, dload;
   qload.init(P.q_tok, w, lane);
   dload.init((int64_t)P.Hq * D, w, lane);
   auto issue = [&](const Cursor& cu, int buf) {
     const int hx = g * P.R + cu.e;
     const int q0 = (sld(P.t.ent + cu.it) & 0x7fffffff) * BM;
-    qload.issue(smem + (2 * buf) * TILE, P.q + (int64_t)hx * P.q_head, P.q_tok, q0, P.Tq, w, lane);
-    dload.issue(smem + (2 * buf + 1) * TILE, P.d_o + (int64_t)hx * D, (int64_t)P.Hq * D, q0, P.Tq, w, lane);
+    qload.issue(smem_lds + (2 * buf) * TILE * 2, P.q + (int64_t)hx * P.q_head, P.q_tok, q0, P.Tq, w, lane);
+    dload.issue(smem_lds + (2 * buf + 1) * TILE * 2, P.d_o + (int64_t)hx * D, (int64_t)P.Hq * D, q0, P.Tq, w,
+                lane);
     if (w == 0 && lane < 32) {
       const float* src = (lane < 16 ? P.nlse : P.ndelta) + (int64_t)hx * P.Tq_pad + q0 + 4 * (lane & 15);
-      g2lds16(src, &rowv[buf][0]);
+      g2lds16(src, rowv_lds + buf * 2 * BM * 4);
     }
   };
   // The K / V register loads complete before the first tiles are requested:

@@ -38,20 +38,23 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
   const int h = g * P.R + e;
   const int qt = sld(P.t.order + rank);
   const int mg = h / P.grp_div;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, li = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, li = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, wave-uniform
   const int row_base = qt * BM + w * 64;
 
   const int32_t* ptr = P.t.ptr + (int64_t)mg * (P.t.nmajor + 1);
   const int beg = sld(ptr + qt), end = sld(ptr + qt + 1);
   const bf16* kg = P.k + (int64_t)g * P.k_head;
   const bf16* vg = P.v + (int64_t)g * P.v_head;
+  const uint32_t smem_lds = lds_addr(smem);
   TileLoader<D, TILE_ROWS, 2, true> kload;
   TileLoader<D, TILE_TR, 2, false> vload;
   kload.init(P.k_tok, w, lane);
   vload.init(P.v_tok, w, lane);
   auto issue = [&](int kt, int buf) {
-    kload.issue(smem + buf * (KT + VT), kg, P.k_tok, kt * BN, P.Tk, w, lane);
-    vload.issue(smem + buf * (KT + VT) + KT, vg, P.v_tok, kt * BN, P.Tk, w, lane);
+    const uint32_t kl = smem_lds + buf * (KT + VT) * 2;
+    kload.issue(kl, kg, P.k_tok, kt * BN, P.Tk, w, lane);
+    vload.issue(kl + KT * 2, vg, P.v_tok, kt * BN, P.Tk, w, lane);
   };
   if (beg < end) issue(sld(P.t.ent + beg) & 0x7fffffff, 0);
 

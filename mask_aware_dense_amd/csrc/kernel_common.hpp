@@ -151,8 +151,9 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
   return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
-// Source = base (wave-uniform) + voff (per lane, bytes).
-__device__ __forceinline__ void g2lds16(const void* base, uint32_t voff, const void* lds) {
+// Source = base (wave-uniform) + voff (per lane, bytes); destination = LDS
+// byte address lds (wave-uniform).
+__device__ __forceinline__ void g2lds16(const void* base, uint32_t voff, uint32_t lds) {
   uint32_t save;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -161,11 +162,11 @@ __device__ __forceinline__ void g2lds16(const void* base, uint32_t voff, const v
       "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(save)
-      : "v"(voff), "s"(uniform_ptr(base)), "s"(lds_addr(lds))
+      : "v"(voff), "s"(uniform_ptr(base)), "s"(__builtin_amdgcn_readfirstlane(lds))
       : "memory");
 }
 // Source = per-lane 64-bit address.
-__device__ __forceinline__ void g2lds16(const void* g, const void* lds) {
+__device__ __forceinline__ void g2lds16(const void* g, uint32_t lds) {
   uint32_t save;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -174,7 +175,7 @@ __device__ __forceinline__ void g2lds16(const void* g, const void* lds) {
       "global_load_lds_dwordx4 %1, off\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(save)
-      : "v"(g), "s"(lds_addr(lds))
+      : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
       : "memory");
 }
 // Wait until this wave's outstanding vector-memory operations (including
@@ -224,25 +225,27 @@ struct TileLoader {
       off[i] = (uint32_t)(((int64_t)tile_row(p, PERM) * tok + (c < CPR ? c : 0) * 8) * 2);
     }
   }
-  // g: the tensor's head; tok: its token stride (elements).
-  __device__ __forceinline__ void issue(bf16* lds, const bf16* g, int64_t tok, int r0, int T, int w,
+  // lds: LDS byte address of the tile image; g: the tensor's head; tok: its
+  // token stride (elements); w: the wave index, wave-uniform (only the last
+  // round of instructions may leave some waves idle, and that test is scalar).
+  __device__ __forceinline__ void issue(uint32_t lds, const bf16* g, int64_t tok, int r0, int T, int w,
                                         int lane) const {
     if (r0 + 64 <= T) {
       const char* base = reinterpret_cast<const char*>(g + (int64_t)r0 * tok);
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int ii = i * NW + w;
-        if (ii < SPR) g2lds16(base, off[i], lds + ii * 512);
+        if ((i + 1) * NW <= SPR || ii < SPR) g2lds16(base, off[i], lds + ii * 1024);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int ii = i * NW + w;
-        if (ii < SPR) {
+        if ((i + 1) * NW <= SPR || ii < SPR) {
           const int s = ii * 64 + lane;
           const int p = s / SPR, c = s % SPR;
           const int row = min(r0 + tile_row(p, PERM), T - 1);
-          g2lds16(g + (int64_t)row * tok + (c < CPR ? c : 0) * 8, lds + ii * 512);
+          g2lds16(g + (int64_t)row * tok + (c < CPR ? c : 0) * 8, lds + ii * 1024);
         }
       }
     }
