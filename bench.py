@@ -11,14 +11,19 @@ LongCA-bench section 2.1.1).  Timing follows the pages' protocol of warm-up
 steps before timed steps (appendix A.4: 5 warm-ups, 20 steps).
 
 Default workload: CAUSAL, one packed sequence of 32768 tokens, GQA 64 query
-heads : 8 KV heads, head dim 128.
+heads : 8 KV heads, head dim 128.  Prints one JSON line.
 
-Prints one JSON line.  `--gpus N` with N > 1 is refused: this build runs on
-one GPU.
+`--suite` instead runs every workload family of the path -- the twelve static
+masks at 32K, uniform and variable block-sparse masks at 32K and 128K, and
+ring-step shares at their 8K x 8K shape -- and prints one JSON line per
+workload.
+
+`--gpus N` with N > 1 is refused: this build runs on one GPU.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -33,6 +38,9 @@ if ROOT not in sys.path:
 METRIC = "effective attention TFLOP/s fwd and fwd+bwd (unmasked FLOPs) vs bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_dkdv.hip", "kernel_common.hpp", "plan.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+NAMES = ["fwd", "delta", "dkdv", "dq"]
 
 
 def parse():
@@ -49,9 +57,33 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=96, help="query rows in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fwd-only", action="store_true", help="time only the forward (profiling aid)")
+    ap.add_argument("--suite", action="store_true", help="run every workload family, one JSON line each")
+    ap.add_argument("--only", default="", help="with --suite: comma-separated substrings of workload names")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM byte-counter calibration) and exit")
     return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mask_aware_dense_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources and this workload; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash() or rec.get("workload") != workload:
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else float(k["hbm_bytes_per_launch"])
 
 
 def cpu_baseline(args, q, k, v, do, spec, scale):
@@ -80,6 +112,178 @@ def cpu_baseline(args, q, k, v, do, spec, scale):
     }
 
 
+class Runner:
+    """Times the path on one plan and one set of device tensors."""
+
+    def __init__(self, torch, mad, plan, Tq, Tk, Hq, Hkv, d, seed):
+        from mad_inputs import grad_out, qkv
+        self.torch, self.mad, self.plan = torch, mad, plan
+        dev = torch.device("cuda", 0)
+        q, k, v = qkv(seed, Tq, Tk, Hq, Hkv, d)
+        do = grad_out(seed, Tq, Hq, d)
+        self.host = (q, k, v, do)
+        self.q, self.k, self.v, self.do = (x.to(dev) for x in (q, k, v, do))
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((Hq, Tq), dtype=torch.float32, device=dev)
+        self.dq, self.dk, self.dv = torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v)
+        self.ws = torch.empty(mad.bwd_workspace_bytes(plan, Tq, Tk, Hq, Hkv, d), dtype=torch.uint8, device=dev)
+        self.scale = 1.0 / np.sqrt(d)
+        self.stream = torch.cuda.current_stream()
+
+    def step(self, fwd_only=False, evs=None):
+        mad, s = self.mad, self.stream
+        if evs is not None:
+            evs[0].record(s)
+        mad.attn_fwd(self.plan, self.q, self.k, self.v, self.o, self.lse, self.scale, s)
+        if evs is not None:
+            evs[1].record(s)
+        if fwd_only:
+            return
+        for i, ph in enumerate((mad.BWD_DELTA, mad.BWD_DKDV, mad.BWD_DQ)):
+            mad.attn_bwd_phases(self.plan, self.q, self.k, self.v, self.o, self.do, self.lse, self.dq, self.dk,
+                                self.dv, self.ws, self.scale, ph, s)
+            if evs is not None:
+                evs[2 + i].record(s)
+
+    def time(self, steps, warmup, fwd_only=False):
+        """Returns (wall seconds for `steps` steps, per-kernel mean ms, per-kernel median ms)."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.step(fwd_only)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(steps):
+            self.step(fwd_only, evs[s])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        nk = 1 if fwd_only else 4
+        per = np.array([[evs[s][i].elapsed_time(evs[s][i + 1]) for i in range(nk)] for s in range(steps)])
+        mean = {NAMES[i]: float(np.mean(per[:, i])) for i in range(nk)}
+        med = {NAMES[i]: float(np.median(per[:, i])) for i in range(nk)}
+        return wall, mean, med
+
+
+def roofline(kern_ms, pairs, d, T, Hq, workload):
+    """Roofline entry of the dominant kernel (largest mean time).
+
+    Algorithmic work per launch: forward 4d FLOP per unmasked (query, key,
+    head) pair; dK/dV kernel 8d (its S, dP, dV, dK products); dQ kernel 2d
+    (its dQ product -- its S and dP are recomputed, not algorithmic); the
+    delta pre-pass is HBM-bound (reads O and dO, writes two fp32 rows).
+    """
+    alg = {"fwd": 4.0 * d * pairs, "dkdv": 8.0 * d * pairs, "dq": 2.0 * d * pairs}
+    dom = max(kern_ms, key=kern_ms.get)
+    traffic = measured_traffic(dom, workload)
+    if dom == "delta":
+        bytes_ = 2.0 * 2 * T * Hq * d + 8.0 * T * Hq
+        ach = bytes_ / (kern_ms[dom] * 1e-3) / 1e9
+        return {"kernel": "delta", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBS, "traffic": traffic}
+    ach = alg[dom] / (kern_ms[dom] * 1e-3) / 1e12
+    return {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": ach / PEAK_BF16_TFLOPS, "traffic": traffic}
+
+
+# ---------------------------------------------------------------------------
+# Workload suite
+# ---------------------------------------------------------------------------
+def suite_workloads(seed):
+    """(name, builder) pairs; a builder returns (plan, Tq, Tk, Hq, Hkv, d, config dict)."""
+    from mad_inputs import block_scores, doc_lengths, variable_block_sizes
+    T = 32768
+    out = []
+
+    def static(pattern, **kw):
+        def build(mad):
+            sl = mad.mask_slices(pattern, T, **kw)
+            return mad.mask_compile(sl, T, T), T, T, 64, 8, 128, {"mask": pattern, "seq_len": T, **{
+                k: (v if not isinstance(v, (list, np.ndarray)) else f"{len(v)} documents") for k, v in kw.items()}}
+        return build
+
+    docs = [int(x) for x in doc_lengths(seed, T)]
+    for pattern, kw in [
+        ("FULL", {}), ("CAUSAL", {}), ("SLIDING_WINDOW", {"window": 4096}),
+        ("FULL_DOCUMENT", {"doc_lens": docs}), ("CAUSAL_DOCUMENT", {"doc_lens": docs}),
+        ("SLIDING_WINDOW_CAUSAL_DOCUMENT", {"window": 4096, "doc_lens": docs}),
+        ("PREFIX_LM", {}), ("SHARED_QUESTION", {"question": 2048, "n_answers": 4}),
+        ("GLOBAL_SLIDING", {"global_len": 256, "window": 2048}), ("CAUSAL_BLOCKWISE", {"block": 2048}),
+        ("BLOCK_CAUSAL_DOCUMENT", {"block": 1024, "doc_lens": docs}), ("PREFIX_LM_DOCUMENT", {"doc_lens": docs}),
+    ]:
+        out.append((f"{pattern} 32K GQA 64:8", static(pattern, **kw)))
+
+    def sparse(S, Hq, Hkv, b, pct, variable):
+        def build(mad):
+            G = Hkv  # one keep set per KV-head group (per head for MHA)
+            if variable:
+                sizes = variable_block_sizes(seed, S, 32, 256)
+                edges = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+            else:
+                edges = np.arange(0, S + 1, b, dtype=np.int32)
+            n = len(edges) - 1
+            keep = mad.block_topk(block_scores(seed, G, n, n), pct)
+            plan = mad.sparse_plan(G, edges, edges, keep)
+            return plan, S, S, Hq, Hkv, 128, {
+                "mask": "VARIABLE_BLOCK_SPARSE" if variable else "BLOCK_SPARSE", "seq_len": S,
+                "block": "U{32..256}" if variable else b, "sparsity": pct / 100.0, "keep_groups": G}
+        return build
+
+    for S, Hq, Hkv, b, pct, var in [
+        (32768, 64, 8, 128, 20, False), (32768, 64, 8, 128, 50, False), (32768, 64, 8, 128, 80, False),
+        (32768, 64, 8, 64, 50, False), (32768, 64, 64, 64, 80, False), (32768, 64, 8, 0, 50, True),
+        (131072, 64, 8, 128, 20, False),
+    ]:
+        tag = "variable" if var else f"b{b}"
+        heads = "MHA 64:64" if Hq == Hkv else f"GQA {Hq}:{Hkv}"
+        out.append((f"BLOCK_SPARSE {S // 1024}K {heads} {tag} s{pct / 100:.1f}", sparse(S, Hq, Hkv, b, pct, var)))
+
+    def ring(layout, rank, source):
+        def build(mad):
+            C = 8192
+            sl = mad.ring_step_slices(layout, 12, C, rank, source)
+            return mad.mask_compile(sl, C, C), C, C, 64, 8, 128, {
+                "mask": "RING_STEP", "layout": layout, "n_ranks": 12, "rank": rank, "source": source,
+                "chunk": C}
+        return build
+
+    for layout, rank, source in [("contiguous", 11, 0), ("contiguous", 11, 11), ("headtail", 0, 0),
+                                 ("headtail", 0, 5)]:
+        out.append((f"RING_STEP {layout} r{rank} s{source} 8K", ring(layout, rank, source)))
+    return out
+
+
+def run_suite(args, torch, mad):
+    only = [s.strip() for s in args.only.split(",") if s.strip()]
+    for name, build in suite_workloads(args.seed):
+        if only and not any(o in name for o in only):
+            continue
+        print(f"workload: {name}", file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        plan, Tq, Tk, Hq, Hkv, d, cfg = build(mad)
+        plan_s = time.perf_counter() - t0
+        plan.upload()
+        st = plan.stats(0)
+        G = len(st["pairs"])
+        pairs = int(sum(int(x) for x in st["pairs"]) * (Hq // G))
+        r = Runner(torch, mad, plan, Tq, Tk, Hq, Hkv, d, args.seed)
+        wall, mean, med = r.time(args.steps, args.warmup)
+        t_fwd = mean["fwd"] * 1e-3
+        fwdbwd = 14.0 * d * pairs * args.steps / wall / 1e12
+        rec = {
+            "workload": name, "metric": METRIC, "unit": "TFLOP/s", "value": fwdbwd,
+            "fwd_tflops": 4.0 * d * pairs / t_fwd / 1e12, "fwdbwd_frac_peak": fwdbwd / PEAK_BF16_TFLOPS,
+            "ms_per_step": wall * 1e3 / args.steps, "kernel_ms_mean": mean, "kernel_ms_median": med,
+            "unmasked_pairs": pairs, "density": pairs / (float(Tq) * Tk * Hq), "plan_compile_s": plan_s,
+            "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": name, **cfg, "heads_q": Hq, "heads_kv": Hkv, "head_dim": d},
+            "roofline": roofline(mean, pairs, d, Tq, Hq, name),
+        }
+        print(json.dumps(rec), flush=True)
+        del r, plan
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -97,89 +301,31 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}))
         return
     import mask_aware_dense_amd as mad
-    from mad_inputs import grad_out, qkv
     from oracle import masks as M
 
+    torch.cuda.set_device(torch.device("cuda", 0))
+    if args.suite:
+        run_suite(args, torch, mad)
+        return
+
     T, Hq, Hkv, d = args.seq, args.hq, args.hkv, args.d
-    scale = 1.0 / np.sqrt(d)
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-
-    q, k, v = qkv(args.seed, T, T, Hq, Hkv, d)
-    do = grad_out(args.seed, T, Hq, d)
-    qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
-
     slices = mad.mask_slices(args.mask, T)
     t0 = time.perf_counter()
     plan = mad.mask_compile(slices, T, T)
     compile_s = time.perf_counter() - t0
     plan.upload()
-    st = plan.stats(0)
-    pairs_per_head = int(st["pairs"][0])
-    pairs = pairs_per_head * Hq
+    pairs = int(plan.stats(0)["pairs"][0]) * Hq
     flop_fwd = 4.0 * d * pairs
     flop_bwd = 10.0 * d * pairs
 
-    o = torch.empty_like(qd)
-    lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
-    ws = torch.empty(mad.bwd_workspace_bytes(plan, T, T, Hq, Hkv, d), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
-    names = ["fwd", "delta", "dkdv", "dq"]
-
-    def step(evs=None):
-        if evs is not None:
-            evs[0].record(stream)
-        mad.attn_fwd(plan, qd, kd, vd, o, lse, scale, stream)
-        if evs is not None:
-            evs[1].record(stream)
-        if args.fwd_only:
-            return
-        for i, ph in enumerate((mad.BWD_DELTA, mad.BWD_DKDV, mad.BWD_DQ)):
-            mad.attn_bwd_phases(plan, qd, kd, vd, o, dod, lse, dq, dk, dv, ws, scale, ph, stream)
-            if evs is not None:
-                evs[2 + i].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(evs[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    nk = 1 if args.fwd_only else 4
-    per = np.array([[evs[s][i].elapsed_time(evs[s][i + 1]) for i in range(nk)] for s in range(args.steps)])
-    kern_ms = {names[i]: float(np.mean(per[:, i])) for i in range(nk)}
-    kern_med = {names[i]: float(np.median(per[:, i])) for i in range(nk)}
+    r = Runner(torch, mad, plan, T, T, Hq, Hkv, d, args.seed)
+    wall, kern_ms, kern_med = r.time(args.steps, args.warmup, args.fwd_only)
     ms_step = wall * 1e3 / args.steps
-    t_fwd = kern_ms["fwd"] * 1e-3
-    fwd_tflops = flop_fwd / t_fwd / 1e12
-    if args.fwd_only:
-        value = fwd_tflops
-    else:
-        value = (flop_fwd + flop_bwd) * args.steps / wall / 1e12
+    fwd_tflops = flop_fwd / (kern_ms["fwd"] * 1e-3) / 1e12
+    value = fwd_tflops if args.fwd_only else (flop_fwd + flop_bwd) * args.steps / wall / 1e12
+    workload = (f"{args.mask} attention {'fwd' if args.fwd_only else 'fwd+bwd'}, packed batch 1, "
+                f"T={T}, GQA {Hq}:{Hkv}, head_dim {d}")
 
-    # Dominant kernel and its algorithmic work per launch: forward 4d FLOP per
-    # unmasked (query, key, head) pair; dK/dV kernel 8d (S, dP, dV, dK
-    # products); dQ kernel 2d (its dQ product -- its S and dP are recomputed,
-    # not algorithmic); the delta pre-pass is HBM-bound (reads O and dO).
-    alg = {"fwd": 4.0 * d * pairs, "dkdv": 8.0 * d * pairs, "dq": 2.0 * d * pairs}
-    dom = max(kern_ms, key=kern_ms.get)
-    if dom == "delta":
-        bytes_ = 2.0 * 2 * T * Hq * d + 4.0 * T * Hq
-        ach = bytes_ / (kern_ms[dom] * 1e-3) / 1e9
-        roof = {"kernel": "delta", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": ach / PEAK_HBM_GBS, "traffic": None}
-    else:
-        ach = alg[dom] / (kern_ms[dom] * 1e-3) / 1e12
-        roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": ach / PEAK_BF16_TFLOPS, "traffic": None}
-
-    spec = M.MaskSpec(args.mask, T, T)
     out = {
         "metric": METRIC,
         "value": value,
@@ -193,10 +339,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{args.mask} attention {'fwd' if args.fwd_only else 'fwd+bwd'}, packed batch 1, "
-                               f"T={T}, GQA {Hq}:{Hkv}, head_dim {d}",
-                   "mask": args.mask, "seq_len": T, "heads_q": Hq, "heads_kv": Hkv, "head_dim": d,
-                   "parallelism": "single GPU"},
+        "config": {"workload": workload, "mask": args.mask, "seq_len": T, "heads_q": Hq, "heads_kv": Hkv,
+                   "head_dim": d, "parallelism": "single GPU"},
         "fwd_tflops": fwd_tflops,
         "fwd_frac_peak": fwd_tflops / PEAK_BF16_TFLOPS,
         "fwdbwd_frac_peak": value / PEAK_BF16_TFLOPS,
@@ -204,10 +348,12 @@ def main():
         "kernel_ms_median": kern_med,
         "unmasked_pairs": pairs,
         "mask_compile_s": compile_s,
-        "roofline": roof,
+        "roofline": roofline(kern_ms, pairs, d, T, Hq, workload),
+        "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args, q, k, v, do, spec, scale)
+        q, k, v, do = r.host
+        out["cpu_baseline"] = cpu_baseline(args, q, k, v, do, M.MaskSpec(args.mask, T, T), 1.0 / np.sqrt(d))
     print(json.dumps(out), flush=True)
 
 

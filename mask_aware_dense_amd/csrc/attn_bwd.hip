@@ -146,8 +146,10 @@ __global__ __launch_bounds__(256) void dq_kernel(const AttnParams P) {
     uint32_t mbits[2] = {0xffffffffu, 0xffffffffu};
     if (masked) {
       const int aux = partial ? sld(P.t.ent_aux + it) : -1;
+      const int r_lo = qt * BM + w * 32;  // the wave's rows, wave-uniform
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) mbits[kb] = keymask32(P.m, aux, mg, partial, row, kt * BN + kb * 32);
+      for (int kb = 0; kb < 2; ++kb)
+        mbits[kb] = keymask32(P.m, aux, mg, partial, row, kt * BN + kb * 32, r_lo, r_lo + 31);
       wait_vmem();
     }
     if (it + 1 < end) issue(sld(P.t.ent + it + 1) & 0x7fffffff, buf ^ 1);

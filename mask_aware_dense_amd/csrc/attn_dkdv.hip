@@ -121,7 +121,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
     // never wait behind them.
     uint32_t mw[2] = {0u, 0u};
     if (partial) {
-      const uint64_t rows = rowmask64(P.m, sld(P.t.ent_aux + cur.it), mg, key, q0);
+      const int k_lo = kt * BN + w * 32;  // the wave's keys, wave-uniform
+      const uint64_t rows = rowmask64(P.m, sld(P.t.ent_aux + cur.it), mg, key, q0, k_lo, k_lo + 31);
       mw[0] = (uint32_t)(rows >> (4 * hh));
       mw[1] = (uint32_t)(rows >> (32 + 4 * hh));
       wait_vmem();

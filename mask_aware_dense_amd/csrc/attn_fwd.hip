@@ -94,7 +94,8 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-          mbits[b][kb] = keymask32(P.m, aux, mg, partial, row_base + b * 32 + li, kt * BN + kb * 32);
+          mbits[b][kb] = keymask32(P.m, aux, mg, partial, row_base + b * 32 + li, kt * BN + kb * 32, row_base,
+                                   row_base + 63);
       wait_vmem();
     }
     if (it + 1 < end) issue(sld(P.t.ent + it + 1) & 0x7fffffff, buf ^ 1);

@@ -274,9 +274,12 @@ __device__ __forceinline__ uint32_t range_bits(int a, int b) {
 // as a bitmask (bit j <-> key key0 + j).  FULL tiles allow every in-range
 // key; PARTIAL tiles evaluate the mask source: the tile's slice list (SLICES)
 // or the block keep bitmap (BLOCKS).  Keys >= Tk and rows >= Tq are never
-// allowed.
+// allowed.  [row_lo, row_hi] is the wave-uniform row range of the calling
+// wave (it contains i): the query / key blocks it meets, their edges and
+// their keep bits are the same for every lane, so they are read with scalar
+// loads and each lane only compares its row against the block edges.
 __device__ __forceinline__ uint32_t keymask32(const MaskDev& m, int32_t aux, int32_t grp, bool partial, int i,
-                                              int key0) {
+                                              int key0, int row_lo, int row_hi) {
   uint32_t bits;
   if (!partial) {
     bits = 0xffffffffu;
@@ -299,13 +302,18 @@ __device__ __forceinline__ uint32_t keymask32(const MaskDev& m, int32_t aux, int
     }
   } else {
     bits = 0u;
-    const int kend = min(key0 + 32, m.Tk) - 1;
-    if (i < m.Tq && key0 <= kend) {
-      const int qb = m.row_qb[i];
-      const int ka = m.col_kb[key0], kz = m.col_kb[kend];
-      const uint64_t* row = m.keep + ((size_t)grp * m.n_qb + qb) * m.nw;
-      for (int kb = ka; kb <= kz; ++kb)
-        if ((row[kb >> 6] >> (kb & 63)) & 1ull) bits |= range_bits(m.k_edges[kb] - key0, m.k_edges[kb + 1] - key0);
+    const int kend = min(key0 + 32, m.Tk) - 1, rhi = min(row_hi, m.Tq - 1);
+    if (key0 <= kend && row_lo <= rhi) {
+      const int qa = sld(m.row_qb + row_lo), qz = sld(m.row_qb + rhi);
+      const int ka = sld(m.col_kb + key0), kz = sld(m.col_kb + kend);
+      for (int qb = qa; qb <= qz; ++qb) {
+        const uint64_t* krow = m.keep + ((size_t)grp * m.n_qb + qb) * m.nw;
+        uint32_t kbits = 0u;  // kept keys of query block qb in this 32-key range
+        for (int kb = ka; kb <= kz; ++kb)
+          if ((sld(krow + (kb >> 6)) >> (kb & 63)) & 1ull)
+            kbits |= range_bits(sld(m.k_edges + kb) - key0, sld(m.k_edges + kb + 1) - key0);
+        if (i >= sld(m.q_edges + qb) && i < sld(m.q_edges + qb + 1)) bits = kbits;
+      }
     }
   }
   const int nvalid = m.Tk - key0;
@@ -325,8 +333,11 @@ __device__ __forceinline__ uint64_t range_bits64(int a, int b) {
 // Allowed query rows among [row0, row0 + 64) for key j of a visited PARTIAL
 // tile of the dK/dV tiling, as a bitmask (bit r <-> row row0 + r): the same
 // predicate as keymask32, read along the key's column.  Rows >= Tq and keys
-// >= Tk are never allowed.
-__device__ __forceinline__ uint64_t rowmask64(const MaskDev& m, int32_t aux, int32_t grp, int j, int row0) {
+// >= Tk are never allowed.  [key_lo, key_hi] is the wave-uniform key range
+// of the calling wave (it contains j); as in keymask32 the block structure
+// is read with scalar loads.
+__device__ __forceinline__ uint64_t rowmask64(const MaskDev& m, int32_t aux, int32_t grp, int j, int row0,
+                                              int key_lo, int key_hi) {
   uint64_t bits = 0ull;
   if (j < m.Tk) {
     if (m.mode == MODE_SLICES) {
@@ -346,14 +357,18 @@ __device__ __forceinline__ uint64_t rowmask64(const MaskDev& m, int32_t aux, int
         bits |= range_bits64(lo - row0, hi - row0);
       }
     } else {
-      const int rlast = min(row0 + 63, m.Tq - 1);
-      if (row0 <= rlast) {
+      const int rlast = min(row0 + 63, m.Tq - 1), khi = min(key_hi, m.Tk - 1);
+      if (row0 <= rlast && key_lo <= khi) {
         const int qa = sld(m.row_qb + row0), qz = sld(m.row_qb + rlast);
-        const int kb = m.col_kb[j];
-        for (int qb = qa; qb <= qz; ++qb) {
-          const uint64_t* row = m.keep + ((size_t)grp * m.n_qb + qb) * m.nw;
-          if ((row[kb >> 6] >> (kb & 63)) & 1ull)
-            bits |= range_bits64(sld(m.q_edges + qb) - row0, sld(m.q_edges + qb + 1) - row0);
+        const int ka = sld(m.col_kb + key_lo), kz = sld(m.col_kb + khi);
+        for (int kb = ka; kb <= kz; ++kb) {
+          uint64_t rbits = 0ull;  // rows of the query blocks that keep key block kb
+          for (int qb = qa; qb <= qz; ++qb) {
+            const uint64_t* krow = m.keep + ((size_t)grp * m.n_qb + qb) * m.nw;
+            if ((sld(krow + (kb >> 6)) >> (kb & 63)) & 1ull)
+              rbits |= range_bits64(sld(m.q_edges + qb) - row0, sld(m.q_edges + qb + 1) - row0);
+          }
+          if (j >= sld(m.k_edges + kb) && j < sld(m.k_edges + kb + 1)) bits = rbits;
         }
       }
     }
