@@ -66,20 +66,58 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
     dva[db] = f32x16{};
   }
 
-  // Flattened walk over (query head of the group, query tile of that head's
-  // list), kept as two cursors: the item being computed and the next one,
-  // whose tiles are prefetched.
+  // Walk over the items (query head e of the group, position `it` in that
+  // head's visit list), kept as two cursors: the item being computed and the
+  // next one, whose tiles are prefetched.  When every query head of the group
+  // uses the same mask group (hence the same list), the list is walked from
+  // its end with the heads innermost: all workgroups then start at the last
+  // query tile and move down through the same tiles at the same pace, so the
+  // workgroups running together read the same Q / dO tiles and share them in
+  // L2 (walking up from each key tile's first tile would spread them apart).
+  // Otherwise each head's list is walked in turn.
   struct Cursor {
-    int e, it, end;
+    int e, it, end;  // shared list: `it` runs down to `end` (the list start)
+    bool ok;
   };
+  const int h0 = g * P.R;
+  const bool shared = (h0 / P.grp_div) == ((h0 + P.R - 1) / P.grp_div);
   auto head_list = [&](int e, Cursor& cu) {
-    const int32_t* ptr = P.t.ptr + (int64_t)((g * P.R + e) / P.grp_div) * (P.t.nmajor + 1);
+    const int32_t* ptr = P.t.ptr + (int64_t)((h0 + e) / P.grp_div) * (P.t.nmajor + 1);
     cu.e = e;
     cu.it = sld(ptr + kt);
     cu.end = sld(ptr + kt + 1);
   };
   auto settle = [&](Cursor& cu) {  // move past exhausted heads
     while (cu.it >= cu.end && cu.e + 1 < P.R) head_list(cu.e + 1, cu);
+    cu.ok = cu.it < cu.end;
+  };
+  auto first = [&]() {
+    Cursor cu;
+    head_list(0, cu);
+    if (shared) {
+      const int list_begin = cu.it;
+      cu.it = cu.end - 1;
+      cu.end = list_begin;
+      cu.ok = cu.it >= cu.end;
+    } else {
+      settle(cu);
+    }
+    return cu;
+  };
+  auto advance = [&](Cursor cu) {
+    if (shared) {
+      if (cu.e + 1 < P.R) {
+        ++cu.e;
+      } else {
+        cu.e = 0;
+        --cu.it;
+      }
+      cu.ok = cu.it >= cu.end;
+    } else {
+      ++cu.it;
+      settle(cu);
+    }
+    return cu;
   };
   const uint32_t smem_lds = lds_addr(smem), rowv_lds = lds_addr(&rowv[0][0]);
   TileLoader<D, TILE_MIXED, 4, false> qload, dload;
@@ -99,21 +137,17 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
   // The K / V register loads complete before the first tiles are requested:
   // the loop's waits count the direct loads, which the compiler does not track.
   wait_vmem();
-  Cursor cur;
-  head_list(0, cur);
-  settle(cur);
-  if (cur.it < cur.end) issue(cur, 0);
+  Cursor cur = first();
+  if (cur.ok) issue(cur, 0);
 
-  for (int n = 0; cur.it < cur.end; ++n) {
+  for (int n = 0; cur.ok; ++n) {
     const int buf = n & 1;
     const int h = g * P.R + cur.e;
     const int mg = h / P.grp_div;
     const uint32_t ent = (uint32_t)sld(P.t.ent + cur.it);
     const bool partial = (ent & ENT_PARTIAL) != 0;
     const int q0 = (int)(ent & 0x7fffffffu) * BM;
-    Cursor nxt = cur;
-    ++nxt.it;
-    settle(nxt);
+    const Cursor nxt = advance(cur);
     wait_vmem();
     __syncthreads();
     // Rows of the tile this lane's key may see (PARTIAL tiles), evaluated
@@ -127,7 +161,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
       mw[1] = (uint32_t)(rows >> (32 + 4 * hh));
       wait_vmem();
     }
-    if (nxt.it < nxt.end) issue(nxt, buf ^ 1);
+    if (nxt.ok) issue(nxt, buf ^ 1);
     const bf16* Qs = smem + (2 * buf) * TILE;
     const bf16* Ds = smem + (2 * buf + 1) * TILE;
     const float* nl_s = &rowv[buf][0];
