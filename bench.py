@@ -278,6 +278,7 @@ def run_suite(args, torch, mad):
             "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": name, **cfg, "heads_q": Hq, "heads_kv": Hkv, "head_dim": d},
             "roofline": roofline(mean, pairs, d, Tq, Hq, name),
+            "kernel_source_hash": kernel_source_hash(),
         }
         print(json.dumps(rec), flush=True)
         del r, plan
