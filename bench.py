@@ -38,7 +38,7 @@ if ROOT not in sys.path:
 METRIC = "effective attention TFLOP/s fwd and fwd+bwd (unmasked FLOPs) vs bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_dkdv.hip", "kernel_common.hpp", "plan.hpp"]
+KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_dkdv.hip", "ring.hip", "kernel_common.hpp", "plan.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 NAMES = ["fwd", "delta", "dkdv", "dq"]
 
@@ -283,6 +283,67 @@ def run_suite(args, torch, mad):
         print(json.dumps(rec), flush=True)
         del r, plan
         torch.cuda.empty_cache()
+    for layout, rank in [("headtail", 0), ("contiguous", 11)]:
+        name = f"RING 12x8K {layout} rank {rank}: all steps + merge, backward"
+        if only and not any(o in name for o in only):
+            continue
+        print(f"workload: {name}", file=sys.stderr, flush=True)
+        print(json.dumps(ring_share(args, torch, mad, layout, 12, 8192, rank, name)), flush=True)
+        torch.cuda.empty_cache()
+
+
+def ring_share(args, torch, mad, layout, N, C, rank, name, Hq=64, Hkv=8, d=128):
+    """One rank's whole ring share (every step's kernels, the K/V staging copies and the LSE merge
+    in the forward; delta, every step's dK/dV and dQ kernels and the dQ rounding in the backward)."""
+    from mad_inputs import grad_out, qkv
+    dev = torch.device("cuda", 0)
+    q, _, _ = qkv(args.seed, C, 1, Hq, Hkv, d)
+    _, k, v = qkv(args.seed + 1, 1, N * C, Hq, Hkv, d)
+    do = grad_out(args.seed, C, Hq, d)
+    q, k, v, do = (x.to(dev) for x in (q, k, v, do))
+    ring = mad.Ring(layout, N, C, rank, Hq, Hkv, d)
+    info = ring.info()
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq, C), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    scale = 1.0 / np.sqrt(d)
+    s = torch.cuda.current_stream()
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(s)
+        ring.fwd(q, k, v, o, lse, scale, s)
+        if evs:
+            evs[1].record(s)
+        ring.bwd(q, k, v, o, do, lse, dq, dk, dv, scale, s)
+        if evs:
+            evs[2].record(s)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for x in range(args.steps):
+        step(evs[x])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    pairs = info["pairs_per_head"] * Hq
+    value = 14.0 * d * pairs * args.steps / wall / 1e12
+    del ring
+    return {
+        "workload": name, "metric": METRIC, "unit": "TFLOP/s", "value": value,
+        "fwd_tflops": 4.0 * d * pairs / (fwd * 1e-3) / 1e12, "fwdbwd_frac_peak": value / PEAK_BF16_TFLOPS,
+        "ms_per_step": wall * 1e3 / args.steps, "kernel_ms_mean": {"fwd": fwd, "bwd": bwd},
+        "unmasked_pairs": pairs, "density": pairs / (float(C) * N * C * Hq), "n_steps": info["n_steps"],
+        "device_bytes": info["device_bytes"], "steps": args.steps, "warmup": args.warmup, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "mask": "CAUSAL over the ring", "layout": layout, "n_ranks": N, "chunk": C,
+                   "rank": rank, "heads_q": Hq, "heads_kv": Hkv, "head_dim": d},
+        "kernel_source_hash": kernel_source_hash(),
+    }
 
 
 def main():

@@ -229,6 +229,79 @@ mad_status mad_attn_bwd_phases(const mad_plan* plan, const void* q, const void* 
                                int32_t Tk, int32_t Hq, int32_t Hkv, int32_t d, const int64_t* strides,
                                float scale, uint32_t phases, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Log-sum-exp merge of partial attention results (LongCA-bench section 2.3
+ * and the notes' key design 3: ring context parallelism combines, per query
+ * row, the outputs that one rank's queries get from each key chunk).  With
+ * the keys of a row split into disjoint parts t, each giving O_t and LSE_t
+ * over its own keys:
+ *   LSE = ln sum_t exp(LSE_t),   O = sum_t exp(LSE_t - LSE) O_t.
+ * Parts with LSE_t = -inf weigh zero; a row whose parts are all -inf gets
+ * O = 0 and LSE = -inf.
+ *   n_parts    1..32.
+ *   o_parts    host array of n_parts device pointers, each bf16 [Tq, Hq, d]
+ *              packed, 16-byte aligned.
+ *   lse_parts  host array of n_parts device pointers, each fp32 [Hq, Tq].
+ *   o, lse     outputs in the same layouts; o may alias o_parts[t] and lse
+ *              may alias lse_parts[t] (every element is read before it is
+ *              written by the same thread).
+ *   d          64 or 128.
+ * Arithmetic in fp32, O rounded to bf16.  Runs on `stream`; allocates
+ * nothing.  Invalid arguments return MAD_ERR_INVALID / MAD_ERR_UNSUPPORTED
+ * before anything is launched.
+ * ------------------------------------------------------------------------- */
+mad_status mad_lse_merge(int32_t n_parts, const void* const* o_parts, const float* const* lse_parts,
+                         void* o, float* lse, int32_t Tq, int32_t Hq, int32_t d, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * One rank's share of ring context-parallel attention, run on one GPU
+ * (LongCA-bench section 2.3, the notes' key designs 3 and 4).  The causal
+ * sequence of n_ranks * chunk tokens is split over n_ranks ranks in the given
+ * layout (as in mad_ring_step_slices); this object computes what rank `rank`
+ * computes over the n_ranks ring steps, with the K/V chunks that would arrive
+ * from the other ranks taken from a global K/V held on this GPU:
+ *   forward: for each step with a non-empty mask, the source's K/V chunk is
+ *     staged into one of two buffers on a copy stream (the copy of step i+1
+ *     overlaps the kernels of step i), the forward kernel gives (O_t, LSE_t)
+ *     for the local queries, and one LSE merge gives the rank's O and LSE;
+ *   backward: with the merged O / LSE (the pages' rule for ring backward),
+ *     the delta pre-pass runs once, then per step the dK/dV and dQ kernels;
+ *     dQ is accumulated in fp32 over the steps and rounded once, and each
+ *     step's dK / dV (this rank's contribution to the source's keys) is
+ *     written at the source chunk's global position.
+ * Creation compiles one mask plan per step, uploads them to the current
+ * device and allocates every device buffer (K/V staging, per-step partial
+ * outputs, the dQ accumulator, the backward workspace); the fwd / bwd calls
+ * allocate nothing.
+ *   layout     0 = contiguous, 1 = head-tail (chunk even).
+ *   Hq, Hkv, d GQA heads (Hq % Hkv == 0) and head dim (64 or 128).
+ * Tensors (device, bf16, packed, 16-byte aligned): q, o, d_o, dq [chunk, Hq, d]
+ * (the rank's local rows: contiguous -> global rows [rank*chunk, +chunk);
+ * head-tail -> halves rank and 2*n_ranks-1-rank of chunk/2 rows each);
+ * k, v, dk, dv [n_ranks*chunk, Hkv, d] in global order; lse fp32 [Hq, chunk].
+ * dk / dv rows of chunks no step of this rank reads are set to 0.  The
+ * object's buffers are reused by every call: calls on one object must not
+ * overlap.
+ * ------------------------------------------------------------------------- */
+typedef struct mad_ring mad_ring;
+
+mad_status mad_ring_create(int32_t layout, int32_t n_ranks, int32_t chunk, int32_t rank, int32_t Hq,
+                           int32_t Hkv, int32_t d, mad_ring** out);
+
+/* Number of non-empty steps, unmasked (query, key) pairs per head summed over
+ * them, and the device bytes the object holds. */
+mad_status mad_ring_info(const mad_ring* ring, int32_t* n_steps, int64_t* pairs_per_head,
+                         size_t* device_bytes);
+
+mad_status mad_ring_fwd(mad_ring* ring, const void* q, const void* k, const void* v, void* o, float* lse,
+                        float scale, hipStream_t stream);
+
+mad_status mad_ring_bwd(mad_ring* ring, const void* q, const void* k, const void* v, const void* o,
+                        const void* d_o, const float* lse, void* dq, void* dk, void* dv, float scale,
+                        hipStream_t stream);
+
+void mad_ring_destroy(mad_ring* ring);
+
 /* Message describing the last failure on the calling thread ("" if none). */
 const char* mad_last_error(void);
 

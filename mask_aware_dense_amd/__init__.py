@@ -17,7 +17,7 @@ import numpy as np
 __all__ = [
     "MadError", "lib", "Plan", "mask_slices", "ring_step_slices", "block_topk",
     "mask_compile", "sparse_plan", "attn_fwd", "attn_bwd", "attn_bwd_phases", "bwd_workspace_bytes",
-    "BWD_DELTA", "BWD_DKDV", "BWD_DQ", "BWD_ALL",
+    "lse_merge", "Ring", "BWD_DELTA", "BWD_DKDV", "BWD_DQ", "BWD_ALL",
     "PATTERNS", "SLICE_DTYPE",
 ]
 
@@ -75,6 +75,12 @@ _SIGS = {
                             _I32, _I32, _I32, _I32, _I32, _VP, _F32, _VP]),
     "mad_attn_bwd_phases": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
                                    _I32, _I32, _I32, _I32, _I32, _VP, _F32, ctypes.c_uint32, _VP]),
+    "mad_lse_merge": (_I32, [_I32, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _VP]),
+    "mad_ring_create": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_VP)]),
+    "mad_ring_info": (_I32, [_VP, _PI32, _PI64, ctypes.POINTER(ctypes.c_size_t)]),
+    "mad_ring_fwd": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _F32, _VP]),
+    "mad_ring_bwd": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _F32, _VP]),
+    "mad_ring_destroy": (None, [_VP]),
     "mad_last_error": (ctypes.c_char_p, []),
     "mad_version": (ctypes.c_char_p, []),
 }
@@ -265,3 +271,47 @@ def attn_bwd_phases(plan: Plan, q, k, v, o, d_o, lse, dq, dk, dv, workspace, sca
     _check(lib().mad_attn_bwd_phases(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
                                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes, Tq, Tk, Hq, Hkv, d,
                                      st, float(scale), int(phases), _stream(stream)))
+
+
+# --------------------------------------------------------------------------- merge and ring
+
+def lse_merge(o_parts, lse_parts, o, lse, stream=None):
+    """Merge partial results (lists of bf16 [Tq, Hq, d] and fp32 [Hq, Tq] device tensors) into o, lse."""
+    n = len(o_parts)
+    if len(lse_parts) != n:
+        raise ValueError("o_parts and lse_parts differ in length")
+    Tq, Hq, d = o.shape
+    op = (ctypes.c_void_p * max(n, 1))(*[_ptr(x) for x in o_parts])
+    lp = (ctypes.c_void_p * max(n, 1))(*[_ptr(x) for x in lse_parts])
+    _check(lib().mad_lse_merge(n, ctypes.cast(op, _VP), ctypes.cast(lp, _VP), _ptr(o), _ptr(lse), Tq, Hq, d,
+                               _stream(stream)))
+
+
+class Ring:
+    """Owner of one rank's ring context-parallel share (mad_ring*)."""
+
+    def __init__(self, layout, n_ranks: int, chunk: int, rank: int, Hq: int, Hkv: int, d: int):
+        lid = {"contiguous": 0, "headtail": 1}[layout] if isinstance(layout, str) else int(layout)
+        h = ctypes.c_void_p()
+        _check(lib().mad_ring_create(lid, n_ranks, chunk, rank, Hq, Hkv, d, ctypes.byref(h)))
+        self.handle = h.value
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            lib().mad_ring_destroy(self.handle)
+            self.handle = None
+
+    def info(self) -> dict:
+        n = ctypes.c_int32(0)
+        p = ctypes.c_int64(0)
+        b = ctypes.c_size_t(0)
+        _check(lib().mad_ring_info(self.handle, ctypes.byref(n), ctypes.byref(p), ctypes.byref(b)))
+        return {"n_steps": n.value, "pairs_per_head": p.value, "device_bytes": b.value}
+
+    def fwd(self, q, k, v, o, lse, scale: float, stream=None):
+        _check(lib().mad_ring_fwd(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), float(scale),
+                                  _stream(stream)))
+
+    def bwd(self, q, k, v, o, d_o, lse, dq, dk, dv, scale: float, stream=None):
+        _check(lib().mad_ring_bwd(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(dq),
+                                  _ptr(dk), _ptr(dv), float(scale), _stream(stream)))

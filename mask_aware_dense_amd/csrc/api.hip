@@ -231,17 +231,20 @@ extern "C" mad_status mad_bwd_workspace_bytes(const mad_plan* p, int32_t Tq, int
   return MAD_OK;
 }
 
-extern "C" mad_status mad_attn_bwd_phases(const mad_plan* p, const void* q, const void* k, const void* v,
-                                          const void* o, const void* d_o, const float* lse, void* dq, void* dk,
-                                          void* dv, void* workspace, size_t ws_bytes, int32_t Tq, int32_t Tk,
-                                          int32_t Hq, int32_t Hkv, int32_t d, const int64_t* strides, float scale,
-                                          uint32_t phases, hipStream_t stream) {
-  clear_error();
+namespace mad {
+// The backward with an optional fp32 dQ accumulator (dq_acc, [Tq, Hq, d]):
+// when it is given, the dQ kernel adds its result there and dq is not used.
+mad_status attn_bwd_impl(const mad_plan* p, const void* q, const void* k, const void* v, const void* o,
+                         const void* d_o, const float* lse, void* dq, float* dq_acc, void* dk, void* dv,
+                         void* workspace, size_t ws_bytes, int32_t Tq, int32_t Tk, int32_t Hq, int32_t Hkv, int32_t d,
+                         const int64_t* strides, float scale, uint32_t phases, hipStream_t stream) {
   if (phases == 0 || (phases & ~(uint32_t)MAD_BWD_ALL)) return fail(MAD_ERR_INVALID, "mad_attn_bwd: bad phase set");
   Strides st;
   mad_status s = check_common("mad_attn_bwd", p, q, k, v, Tq, Tk, Hq, Hkv, d, strides, st);
   if (s != MAD_OK) return s;
-  if (Tq > 0 && (!o || !d_o || !lse || !dq)) return fail(MAD_ERR_INVALID, "mad_attn_bwd: o/d_o/lse/dq must not be NULL");
+  if (Tq > 0 && (!o || !d_o || !lse || (!dq && !dq_acc)))
+    return fail(MAD_ERR_INVALID, "mad_attn_bwd: o/d_o/lse/dq must not be NULL");
+  if ((uintptr_t)dq_acc & 15u) return fail(MAD_ERR_UNSUPPORTED, "mad_attn_bwd: dq accumulator must be 16-byte aligned");
   if (Tk > 0 && (!dk || !dv)) return fail(MAD_ERR_INVALID, "mad_attn_bwd: dk/dv must not be NULL");
   if (!aligned16(o) || !aligned16(d_o) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3u))
     return fail(MAD_ERR_UNSUPPORTED, "mad_attn_bwd: o/d_o/dq/dk/dv must be 16-byte and lse 4-byte aligned");
@@ -260,6 +263,7 @@ extern "C" mad_status mad_attn_bwd_phases(const mad_plan* p, const void* q, cons
   Pq.ndelta = (float*)workspace;
   Pq.nlse = (float*)workspace + (size_t)Hq * Pq.Tq_pad;
   Pq.dq = (bf16*)dq;
+  Pq.dq_acc = dq_acc;
   Pq.dk = (bf16*)dk;
   Pq.dv = (bf16*)dv;
   AttnParams Pkv = Pq;
@@ -270,6 +274,17 @@ extern "C" mad_status mad_attn_bwd_phases(const mad_plan* p, const void* q, cons
   hipError_t e = launch_bwd(Pq, Pkv, d, (int)nq, (int)nkv, phases, stream);
   if (e != hipSuccess) return hip_fail("mad_attn_bwd: launch", e);
   return MAD_OK;
+}
+}  // namespace mad
+
+extern "C" mad_status mad_attn_bwd_phases(const mad_plan* p, const void* q, const void* k, const void* v,
+                                          const void* o, const void* d_o, const float* lse, void* dq, void* dk,
+                                          void* dv, void* workspace, size_t ws_bytes, int32_t Tq, int32_t Tk,
+                                          int32_t Hq, int32_t Hkv, int32_t d, const int64_t* strides, float scale,
+                                          uint32_t phases, hipStream_t stream) {
+  clear_error();
+  return attn_bwd_impl(p, q, k, v, o, d_o, lse, dq, nullptr, dk, dv, workspace, ws_bytes, Tq, Tk, Hq, Hkv, d, strides,
+                       scale, phases, stream);
 }
 
 extern "C" mad_status mad_attn_bwd(const mad_plan* p, const void* q, const void* k, const void* v, const void* o,

@@ -230,7 +230,22 @@ __global__ __launch_bounds__(256) void dq_kernel(const AttnParams P) {
   }
 
   // dQ^T: lane holds query row `row`, column d = db*32 + 8(r/4) + 4hh + r%4.
-  if (row < P.Tq) {
+  if (row < P.Tq && P.dq_acc) {
+    // Accumulating form (one call per key chunk): each element has one owner lane.
+    float* dst = P.dq_acc + ((int64_t)row * P.Hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        float4* p4 = reinterpret_cast<float4*>(dst + db * 32 + 8 * rg + 4 * hh);
+        float4 v4 = *p4;
+        v4.x += acc[db][4 * rg + 0] * P.scale;
+        v4.y += acc[db][4 * rg + 1] * P.scale;
+        v4.z += acc[db][4 * rg + 2] * P.scale;
+        v4.w += acc[db][4 * rg + 3] * P.scale;
+        *p4 = v4;
+      }
+  } else if (row < P.Tq) {
     bf16* dst = P.dq + ((int64_t)row * P.Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)

@@ -43,6 +43,7 @@ struct AttnParams {
   float* nlse;        // backward: -LSE / scale, -inf for empty / padded rows, [Hq, Tq_pad]
   int32_t Tq_pad;     // Tq rounded up to a multiple of 128
   bf16* dq;
+  float* dq_acc;      // backward: if set, dQ is added into this fp32 [Tq, Hq, D] buffer instead of written to dq
   bf16* dk;
   bf16* dv;
   int64_t q_tok, q_head, k_tok, k_head, v_tok, v_head;

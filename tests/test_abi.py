@@ -121,3 +121,33 @@ def test_attention_argument_errors_launch_nothing():
     L = mad.lib()
     assert L.mad_attn_fwd(None, None, None, None, None, None, 1, 1, 1, 1, 64, None, ctypes.c_float(1.0), None) == 1
     assert b"plan is NULL" in L.mad_last_error()
+
+
+def test_merge_and_ring_errors():
+    """Argument checks of the LSE merge and the ring object fail before any device work."""
+    L = mad.lib()
+    null = ctypes.c_void_p(0)
+    arr = (ctypes.c_void_p * 1)(0)
+    # n_parts out of range, bad head dim, NULL part arrays
+    assert L.mad_lse_merge(0, arr, arr, null, null, 4, 2, 128, null) == 1
+    assert L.mad_lse_merge(33, arr, arr, null, null, 4, 2, 128, null) == 1
+    assert L.mad_lse_merge(1, arr, arr, null, null, 4, 2, 96, null) == 2
+    assert L.mad_lse_merge(1, null, null, null, null, 4, 2, 128, null) == 1
+    assert L.mad_lse_merge(1, arr, arr, null, null, 4, 0, 128, null) == 1
+    # a NULL part pointer with a real output
+    assert L.mad_lse_merge(1, arr, arr, ctypes.c_void_p(256), ctypes.c_void_p(256), 4, 2, 128, null) == 1
+    assert b"part" in L.mad_last_error()
+    h = ctypes.c_void_p()
+    for args, st in [((2, 4, 64, 0, 4, 2, 128), 1),   # layout
+                     ((0, 0, 64, 0, 4, 2, 128), 1),   # n_ranks
+                     ((0, 33, 64, 0, 4, 2, 128), 1),
+                     ((1, 4, 63, 0, 4, 2, 128), 1),   # odd head-tail chunk
+                     ((0, 4, 64, 4, 4, 2, 128), 1),   # rank
+                     ((0, 4, 64, 0, 4, 3, 128), 1),   # Hq % Hkv
+                     ((0, 4, 64, 0, 4, 2, 80), 2)]:   # head dim
+        assert L.mad_ring_create(*args, ctypes.byref(h)) == st, args
+    assert L.mad_ring_create(0, 4, 64, 0, 4, 2, 128, None) == 1
+    assert L.mad_ring_info(None, None, None, None) == 1
+    assert L.mad_ring_fwd(None, null, null, null, null, null, 1.0, null) == 1
+    assert L.mad_ring_bwd(None, null, null, null, null, null, null, null, null, null, 1.0, null) == 1
+    L.mad_ring_destroy(None)
