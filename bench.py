@@ -38,7 +38,8 @@ if ROOT not in sys.path:
 METRIC = "effective attention TFLOP/s fwd and fwd+bwd (unmasked FLOPs) vs bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_dkdv.hip", "ring.hip", "kernel_common.hpp", "plan.hpp"]
+KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_dkdv.hip", "ring.hip", "blockmask.hip", "kernel_common.hpp",
+                  "plan.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 NAMES = ["fwd", "delta", "dkdv", "dq"]
 
@@ -283,6 +284,14 @@ def run_suite(args, torch, mad):
         print(json.dumps(rec), flush=True)
         del r, plan
         torch.cuda.empty_cache()
+    for S, Hq, Hkv, G, b, pct in [(32768, 64, 8, 8, 128, 50), (131072, 64, 8, 8, 128, 80), (32768, 64, 64, 64, 64, 80)]:
+        heads = "MHA 64:64" if Hq == Hkv else f"GQA {Hq}:{Hkv}"
+        name = f"DYNAMIC BLOCK_SPARSE {S // 1024}K {heads} b{b} s{pct / 100:.1f}: GPU scores + top-k, plan, attention"
+        if only and not any(o in name for o in only):
+            continue
+        print(f"workload: {name}", file=sys.stderr, flush=True)
+        print(json.dumps(dynamic_sparse(args, torch, mad, S, Hq, Hkv, G, b, pct, name)), flush=True)
+        torch.cuda.empty_cache()
     for layout, rank in [("headtail", 0), ("contiguous", 11)]:
         name = f"RING 12x8K {layout} rank {rank}: all steps + merge, backward"
         if only and not any(o in name for o in only):
@@ -290,6 +299,55 @@ def run_suite(args, torch, mad):
         print(f"workload: {name}", file=sys.stderr, flush=True)
         print(json.dumps(ring_share(args, torch, mad, layout, 12, 8192, rank, name)), flush=True)
         torch.cuda.empty_cache()
+
+
+def dynamic_sparse(args, torch, mad, S, Hq, Hkv, G, b, pct, name, d=128):
+    """A dynamic block-sparse mask made from Q and K on the GPU (pooled block scores, top-k), the
+    plan compiled on the host from its keep bitmap, then attention under it."""
+    dev = torch.device("cuda", 0)
+    edges = np.arange(0, S + 1, b, dtype=np.int32)
+    n = len(edges) - 1
+    r = None
+    ws = torch.empty(mad.block_mask_workspace_bytes(G, Hkv, n, n, d), dtype=torch.uint8, device=dev)
+    keep = torch.empty((G, n, (n + 63) // 64), dtype=torch.int64, device=dev)
+    e_d = torch.from_numpy(edges).to(dev)
+    from mad_inputs import qkv
+    q, k, _ = qkv(args.seed, S, S, Hq, Hkv, d)
+    qd, kd = q.to(dev), k.to(dev)
+    scale = 1.0 / np.sqrt(d)
+    for _ in range(2):
+        mad.block_mask(qd, kd, G, e_d, e_d, pct, scale, keep, ws)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(5):
+        mad.block_mask(qd, kd, G, e_d, e_d, pct, scale, keep, ws)
+    ev[1].record()
+    torch.cuda.synchronize()
+    gen_ms = ev[0].elapsed_time(ev[1]) / 5
+    t0 = time.perf_counter()
+    kw = keep.cpu().numpy().view(np.uint64)
+    plan = mad.sparse_plan(G, edges, edges, kw)
+    plan.upload()
+    plan_s = time.perf_counter() - t0
+    del qd, kd
+    st = plan.stats(0)
+    pairs = int(sum(int(x) for x in st["pairs"]) * (Hq // G))
+    r = Runner(torch, mad, plan, S, S, Hq, Hkv, d, args.seed)
+    wall, mean, med = r.time(args.steps, args.warmup)
+    value = 14.0 * d * pairs * args.steps / wall / 1e12
+    del r
+    return {
+        "workload": name, "metric": METRIC, "unit": "TFLOP/s", "value": value,
+        "fwd_tflops": 4.0 * d * pairs / (mean["fwd"] * 1e-3) / 1e12, "fwdbwd_frac_peak": value / PEAK_BF16_TFLOPS,
+        "ms_per_step": wall * 1e3 / args.steps, "kernel_ms_mean": mean, "kernel_ms_median": med,
+        "mask_gen_gpu_ms": gen_ms, "plan_host_s": plan_s, "unmasked_pairs": pairs,
+        "density": pairs / (float(S) * S * Hq), "steps": args.steps, "warmup": args.warmup, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "mask": "BLOCK_SPARSE from pooled block scores", "seq_len": S, "block": b,
+                   "sparsity": pct / 100.0, "keep_groups": G, "heads_q": Hq, "heads_kv": Hkv, "head_dim": d},
+        "kernel_source_hash": kernel_source_hash(),
+    }
 
 
 def ring_share(args, torch, mad, layout, N, C, rank, name, Hq=64, Hkv=8, d=128):

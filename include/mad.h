@@ -230,6 +230,37 @@ mad_status mad_attn_bwd_phases(const mad_plan* plan, const void* q, const void* 
                                float scale, uint32_t phases, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Dynamic block-sparse masks computed on the GPU from Q and K: the coarse
+ * stage of a block-sparse method (LongCA-bench appendix A.3: VSA mean-pools
+ * the QK scores over blocks) followed by appendix A.2's top-k key blocks per
+ * query block.  For mask group g (n_groups groups of Hq / n_groups query
+ * heads; a group's heads must share one KV head, so n_groups must be a
+ * multiple of Hkv), query block qb and key block kb:
+ *   score = scale * (mean of Q over qb's rows and g's heads) . (mean of K over kb's rows)
+ * which equals scale times the mean of q_i . k_j over the block pair and the
+ * group's heads.  Each (g, qb) keeps its k = n_kb - floor(sparsity_pct * n_kb
+ * / 100) (at least 1) highest-scoring key blocks, equal scores in ascending
+ * key-block order (the order mad_block_topk uses).
+ *   q [Tq, Hq, d], k [Tk, Hkv, d]: device bf16, packed, 16-byte aligned.
+ *   q_edges (n_qb + 1) / k_edges (n_kb + 1): device int32, strictly increasing
+ *     from 0 to Tq / Tk (as for mad_sparse_plan); n_kb <= 8192.
+ *   workspace: device, mad_block_mask_workspace_bytes bytes, 256-byte aligned.
+ *   keep: device uint64 [n_groups][n_qb][ceil(n_kb / 64)], fully written; the
+ *     host copy of it is what mad_sparse_plan takes.
+ *   scores: optional device fp32 [n_groups][n_qb][n_kb] (NULL: not written).
+ * Runs on `stream`, allocates nothing; invalid arguments return an error
+ * before anything is launched.
+ * ------------------------------------------------------------------------- */
+mad_status mad_block_mask_workspace_bytes(int32_t n_groups, int32_t Hkv, int32_t n_qb, int32_t n_kb,
+                                          int32_t d, size_t* bytes);
+
+mad_status mad_block_mask(const void* q, const void* k, int32_t Tq, int32_t Tk, int32_t Hq, int32_t Hkv,
+                          int32_t d, int32_t n_groups, const int32_t* q_edges, int32_t n_qb,
+                          const int32_t* k_edges, int32_t n_kb, int32_t sparsity_pct, float scale,
+                          void* workspace, size_t workspace_bytes, uint64_t* keep, float* scores,
+                          hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Log-sum-exp merge of partial attention results (LongCA-bench section 2.3
  * and the notes' key design 3: ring context parallelism combines, per query
  * row, the outputs that one rank's queries get from each key chunk).  With

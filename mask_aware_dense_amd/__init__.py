@@ -17,7 +17,7 @@ import numpy as np
 __all__ = [
     "MadError", "lib", "Plan", "mask_slices", "ring_step_slices", "block_topk",
     "mask_compile", "sparse_plan", "attn_fwd", "attn_bwd", "attn_bwd_phases", "bwd_workspace_bytes",
-    "lse_merge", "Ring", "BWD_DELTA", "BWD_DKDV", "BWD_DQ", "BWD_ALL",
+    "block_mask", "block_mask_workspace_bytes", "lse_merge", "Ring", "BWD_DELTA", "BWD_DKDV", "BWD_DQ", "BWD_ALL",
     "PATTERNS", "SLICE_DTYPE",
 ]
 
@@ -75,6 +75,9 @@ _SIGS = {
                             _I32, _I32, _I32, _I32, _I32, _VP, _F32, _VP]),
     "mad_attn_bwd_phases": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
                                    _I32, _I32, _I32, _I32, _I32, _VP, _F32, ctypes.c_uint32, _VP]),
+    "mad_block_mask_workspace_bytes": (_I32, [_I32, _I32, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)]),
+    "mad_block_mask": (_I32, [_VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _I32, _VP, _I32, _I32, _F32,
+                              _VP, ctypes.c_size_t, _VP, _VP, _VP]),
     "mad_lse_merge": (_I32, [_I32, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _VP]),
     "mad_ring_create": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_VP)]),
     "mad_ring_info": (_I32, [_VP, _PI32, _PI64, ctypes.POINTER(ctypes.c_size_t)]),
@@ -315,3 +318,23 @@ class Ring:
     def bwd(self, q, k, v, o, d_o, lse, dq, dk, dv, scale: float, stream=None):
         _check(lib().mad_ring_bwd(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(dq),
                                   _ptr(dk), _ptr(dv), float(scale), _stream(stream)))
+
+
+# --------------------------------------------------------------------------- dynamic block masks
+
+def block_mask_workspace_bytes(n_groups: int, Hkv: int, n_qb: int, n_kb: int, d: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().mad_block_mask_workspace_bytes(n_groups, Hkv, n_qb, n_kb, d, ctypes.byref(n)))
+    return n.value
+
+
+def block_mask(q, k, n_groups: int, q_edges, k_edges, sparsity_pct: int, scale: float, keep, workspace,
+               scores=None, stream=None):
+    """Keep bitmap (device uint64 tensor [G, n_qb, ceil(n_kb/64)], written) of the top-k key blocks per
+    query block by mean-pooled block scores; q_edges / k_edges are device int32 tensors."""
+    Tq, Hq, d = q.shape
+    Tk, Hkv, _ = k.shape
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().mad_block_mask(_ptr(q), _ptr(k), Tq, Tk, Hq, Hkv, d, n_groups, _ptr(q_edges), q_edges.numel() - 1,
+                                _ptr(k_edges), k_edges.numel() - 1, int(sparsity_pct), float(scale), _ptr(workspace),
+                                nbytes, _ptr(keep), _ptr(scores), _stream(stream)))

@@ -11,6 +11,8 @@ Contents
   tiles      brute-force tile classification (EMPTY / FULL / PARTIAL),
              visit lists and exact pair counts from a dense mask
   merge      log-sum-exp merge of partial attention results
+  blockscore block importance scores from mean-pooled Q and K (dynamic
+             block-sparse masks)
 
 Source: "Long-Context Attention Benchmark: From Kernel Efficiency to
 Distributed Context Parallelism" (LongCA-bench) and its summaries.  The pages
@@ -27,4 +29,4 @@ tests/test_oracle_*.py).  Two mask definitions are this build's readings and
 are parity unpinned as to identity: PREFIX_LM_DOCUMENT (the unnamed sixth
 heterogeneous mask) and CAUSAL_BLOCKWISE (read literally).
 """
-from . import masks, attention, tiles, merge  # noqa: F401
+from . import masks, attention, tiles, merge, blockscore  # noqa: F401

@@ -151,3 +151,29 @@ def test_merge_and_ring_errors():
     assert L.mad_ring_fwd(None, null, null, null, null, null, 1.0, null) == 1
     assert L.mad_ring_bwd(None, null, null, null, null, null, null, null, null, null, 1.0, null) == 1
     L.mad_ring_destroy(None)
+
+
+def test_block_mask_errors():
+    """Argument checks of the GPU block-mask generator fail before any device work."""
+    L = mad.lib()
+    n = ctypes.c_size_t(0)
+    assert L.mad_block_mask_workspace_bytes(8, 8, 16, 16, 128, ctypes.byref(n)) == 0
+    assert n.value == 8 * 16 * 128 * 4 + 8 * 16 * 128 * 4
+    assert L.mad_block_mask_workspace_bytes(8, 8, 16, 16, 96, ctypes.byref(n)) == 2
+    assert L.mad_block_mask_workspace_bytes(0, 8, 16, 16, 128, ctypes.byref(n)) == 1
+    p = ctypes.c_void_p(4096)
+    base = (p, p, 1024, 1024, 8, 2, 128)
+    def call(*over, groups=2, nqb=8, nkb=8, pct=50, ws=1 << 20, **kw):
+        args = list(base)
+        for i, v in over:
+            args[i] = v
+        return L.mad_block_mask(*args, groups, p, nqb, p, nkb, pct, ctypes.c_float(0.1), p, ws, p, None, None)
+    assert call(groups=3) == 1        # does not divide Hq
+    assert call(groups=1) == 1        # group spans two KV heads
+    assert call((6, 80)) == 2         # head dim
+    assert call(pct=101) == 1
+    assert call(nkb=9000) == 1        # more blocks than keys
+    assert call(nqb=0) == 1
+    assert call(ws=16) == 1           # workspace too small
+    assert L.mad_block_mask(None, p, 1024, 1024, 8, 2, 128, 2, p, 8, p, 8, 50, ctypes.c_float(0.1), p, 1 << 20,
+                            p, None, None) == 1
