@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--fwd-only", action="store_true", help="time only the forward (profiling aid)")
     ap.add_argument("--suite", action="store_true", help="run every workload family, one JSON line each")
     ap.add_argument("--only", default="", help="with --suite: comma-separated substrings of workload names")
+    ap.add_argument("--memory", action="store_true",
+                    help="peak device memory of fwd and fwd+bwd over sequence lengths 1K..48K (one JSON line each)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM byte-counter calibration) and exit")
     return ap.parse_args()
@@ -404,6 +406,47 @@ def ring_share(args, torch, mad, layout, N, C, rank, name, Hq=64, Hkv=8, d=128):
     }
 
 
+def run_memory(args, torch, mad):
+    """Peak device memory of the path (LongCA-bench appendix A.4.2): the forward's and the backward's peak,
+    each the bytes of every live tensor (torch's allocator peak) plus the plan's device block, beside the
+    pages' activation model of standard attention, 11bshd + 5bhs^2 + 2bshd bytes."""
+    from mad_inputs import grad_out, qkv
+    dev = torch.device("cuda", 0)
+    for mask, Hq, Hkv in [("GLOBAL_SLIDING", 64, 64), ("CAUSAL", 64, 8)]:
+        for T in [1024, 2048, 4096, 8192, 16384, 32768, 49152]:
+            d = 128
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            base = torch.cuda.memory_allocated()
+            torch.cuda.reset_peak_memory_stats()
+            kw = {"global_len": 256, "window": 2048} if mask == "GLOBAL_SLIDING" else {}
+            plan = mad.mask_compile(mad.mask_slices(mask, T, **kw), T, T)
+            plan.upload()
+            pb = plan.device_bytes()
+            q, k, v = (x.to(dev) for x in qkv(args.seed, T, T, Hq, Hkv, d))
+            o = torch.empty_like(q)
+            lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+            scale = 1.0 / np.sqrt(d)
+            mad.attn_fwd(plan, q, k, v, o, lse, scale)
+            torch.cuda.synchronize()
+            fwd_peak = torch.cuda.max_memory_allocated() - base + pb
+            do = grad_out(args.seed, T, Hq, d).to(dev)
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            ws = torch.empty(mad.bwd_workspace_bytes(plan, T, T, Hq, Hkv, d), dtype=torch.uint8, device=dev)
+            mad.attn_bwd(plan, q, k, v, o, do, lse, dq, dk, dv, ws, scale)
+            torch.cuda.synchronize()
+            bwd_peak = torch.cuda.max_memory_allocated() - base + pb
+            b, sd, hd = 1, T, Hq * d
+            model = 11 * b * sd * hd + 5 * b * Hq * sd * sd + 2 * b * sd * hd
+            rec = {"workload": f"peak memory {mask} {'MHA' if Hq == Hkv else 'GQA'} {Hq}:{Hkv} T={T} d={d}",
+                   "seq_len": T, "mask": mask, "heads_q": Hq, "heads_kv": Hkv, "head_dim": d,
+                   "fwd_peak_bytes": int(fwd_peak), "fwdbwd_peak_bytes": int(bwd_peak), "plan_device_bytes": int(pb),
+                   "standard_attention_activation_model_bytes": int(model),
+                   "note": "peaks count every live tensor of the call (inputs, outputs, workspace) plus the plan"}
+            print(json.dumps(rec), flush=True)
+            del q, k, v, o, lse, do, dq, dk, dv, ws, plan
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -426,6 +469,9 @@ def main():
     torch.cuda.set_device(torch.device("cuda", 0))
     if args.suite:
         run_suite(args, torch, mad)
+        return
+    if args.memory:
+        run_memory(args, torch, mad)
         return
 
     T, Hq, Hkv, d = args.seq, args.hq, args.hkv, args.d

@@ -167,6 +167,12 @@ mad_status mad_plan_upload(mad_plan* plan, hipStream_t stream);
 mad_status mad_plan_stats(const mad_plan* plan, int32_t which, int64_t* pairs_per_group,
                           int64_t* n_full, int64_t* n_partial, int64_t* n_empty);
 
+/* Device bytes the plan holds after mad_plan_upload (0 before): the only
+ * device memory the attention calls use beyond the caller's tensors and
+ * workspace (LongCA-bench appendix A.4.2 and A.5.2 report peak memory; the
+ * mask representation is where FlexAttention spends most of it). */
+mad_status mad_plan_device_bytes(const mad_plan* plan, size_t* bytes);
+
 /* Plan shape: Tq, Tk, number of mask groups, and tile sizes (BM query rows x
  * BN keys) with tile-grid size of tiling `which`.  Any out pointer may be NULL. */
 mad_status mad_plan_info(const mad_plan* plan, int32_t which, int32_t* Tq, int32_t* Tk,

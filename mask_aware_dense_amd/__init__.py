@@ -69,6 +69,7 @@ _SIGS = {
     "mad_plan_info": (_I32, [_VP, _I32, _PI32, _PI32, _PI32, _PI32, _PI32, _PI32, _PI32]),
     "mad_plan_export": (_I32, [_VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP]),
     "mad_plan_destroy": (None, [_VP]),
+    "mad_plan_device_bytes": (_I32, [_VP, ctypes.POINTER(ctypes.c_size_t)]),
     "mad_attn_fwd": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP, _F32, _VP]),
     "mad_bwd_workspace_bytes": (_I32, [_VP, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)]),
     "mad_attn_bwd": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
@@ -181,6 +182,11 @@ class Plan:
     def upload(self, stream=None) -> "Plan":
         _check(lib().mad_plan_upload(self.handle, _stream(stream)))
         return self
+
+    def device_bytes(self) -> int:
+        n = ctypes.c_size_t(0)
+        _check(lib().mad_plan_device_bytes(self.handle, ctypes.byref(n)))
+        return n.value
 
     def info(self, which: int = 0) -> dict:
         v = [ctypes.c_int32() for _ in range(7)]

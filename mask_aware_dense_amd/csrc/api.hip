@@ -181,7 +181,15 @@ extern "C" mad_status mad_plan_upload(mad_plan* p, hipStream_t stream) {
   m.n_kb = p->n_kb;
   m.nw = p->nw;
   p->dev_mem = mem;
+  p->dev_bytes = total;
   p->dev_id = dev;
+  return MAD_OK;
+}
+
+extern "C" mad_status mad_plan_device_bytes(const mad_plan* p, size_t* bytes) {
+  clear_error();
+  if (!p || !bytes) return fail(MAD_ERR_INVALID, "mad_plan_device_bytes: NULL argument");
+  *bytes = p->dev_mem ? p->dev_bytes : 0;
   return MAD_OK;
 }
 

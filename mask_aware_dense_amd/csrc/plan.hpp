@@ -95,6 +95,7 @@ struct mad_plan {
   // device copy (one allocation) and views into it
   void* dev_mem = nullptr;
   int dev_id = -1;
+  size_t dev_bytes = 0;
   mad::TilingDev tdev[2] = {};
   mad::MaskDev mdev = {};
 };
