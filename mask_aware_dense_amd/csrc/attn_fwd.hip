@@ -103,100 +103,172 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
     const bf16* Vs = Ks + KT;
     __builtin_amdgcn_sched_barrier(0);
 
-    // 1. S^T for 2 key blocks x 2 query blocks.
+    // Scores start at 0, or at -inf on masked (row, key) pairs, so masking
+    // costs nothing past this initialisation.  Register r of s[kb][b] holds
+    // key kb*32 + 16(r/8) + 8hh + r%8 of row b*32 + li.
     f32x16 s[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int b = 0; b < 2; ++b) s[kb][b] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = ld16(Ks + (kb * 32 + li) * KRS + (16 * ks + 8 * hh));
-#pragma unroll
-        for (int b = 0; b < 2; ++b) s[kb][b] = mfma32(a, qf[b][ks], s[kb][b]);
-      }
-
-    // 2. Mask (a real branch: FULL tiles must not pay for it).
     if (__builtin_expect(masked, 0)) {
       asm volatile("" ::: "memory");
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = 16 * (r >> 3) + 8 * hh + (r & 7);
-            if (!((mbits[b][kb] >> off) & 1u)) s[kb][b][r] = -INFINITY;
-          }
-    }
-
-    // 3. Online softmax (exp2 domain) with a lagging reference max: each row
-    // keeps a reference m_ref and forms p = exp2(s*c - m_ref).  m_ref moves up
-    // (and the accumulator and sum are rescaled by exp2(m_old - m_new)) only
-    // when the tile's max exceeds m_ref by more than RESCALE_SLACK, so p stays
-    // below 2^RESCALE_SLACK and the rescale is rare.  The result is exact: O
-    // and l share the same reference, and LSE = m_ref + log2(l).
-    constexpr float RESCALE_SLACK = 8.f;
-    float tmax[2];
-    bool need = false;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      float mx = -INFINITY;
-#pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][b][r]);
-      tmax[b] = pair_max(mx) * P.scale_log2;
-      need |= tmax[b] > mrow[b] + RESCALE_SLACK;
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (!((mbits[b][kb] >> (16 * (r >> 3) + 8 * hh + (r & 7))) & 1u)) s[kb][b][r] = -INFINITY;
     }
-    if (__ballot(need)) {
+
+    // LDS operand rings, read two MFMA steps ahead.  Phase-1 step st = (kb,
+    // ks): the K row operand; phase-2 step st = (kb, t2, db): the V^T operand.
+    bf16x8 kr[3], vr[3];
+    auto ldk = [&](int st) {
+      const int kb = st / NKS, ks = st % NKS;
+      kr[st % 3] = ld16(Ks + (kb * 32 + li) * KRS + (16 * ks + 8 * hh));
+    };
+    auto ldv = [&](int st) {
+      const int kb = st / (2 * NDB), t2 = (st / NDB) % 2, db = st % NDB;
+      const int vrow = kb * 32 + 16 * t2 + 8 * hh + tr_row(lane), vcol = db * 32 + tr_col(lane);
+      vr[st % 3] = ld_tr8(Vs + vrow * VRS + vcol, Vs + (vrow + 4) * VRS + vcol);
+    };
+    auto s_step = [&](int st) {  // S^T of key block st / NKS, k-step st % NKS, both query blocks
+      const int kb = st / NKS, ks = st % NKS;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) s[kb][b] = mfma32(kr[st % 3], qf[b][ks], s[kb][b]);
+    };
+    bf16x8 pb[2][2][2];  // P^T operands [kb][t2][b]
+    auto pv_step = [&](int st) {  // O^T += V^T P^T for (kb, t2, db), both query blocks
+      const int kb = st / (2 * NDB), t2 = (st / NDB) % 2, db = st % NDB;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) acc[db][b] = mfma32(vr[st % 3], pb[kb][t2][b], acc[db][b]);
+    };
+    // Online softmax in the exp2 domain against a lagging reference max per
+    // row: p = exp2(s c - m_ref); m_ref moves (and O, l are rescaled by
+    // exp2(m_old - m_new)) only when a key block's max exceeds it by more
+    // than RESCALE_SLACK, so p < 2^RESCALE_SLACK and rescales are rare.  The
+    // result is exact: O and l share the reference and LSE = m_ref + log2 l.
+    constexpr float RESCALE_SLACK = 8.f;
+    float muse[2];
+    auto block_max = [&](int kb, float* tmax) {
+      bool need = false;
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        const float mnew = fmaxf(mrow[b], tmax[b]);
-        const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrow[b] - mnew);
-        mrow[b] = mnew;
-        lrow[b] *= alpha;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][b][r]);
+        tmax[b] = pair_max(mx) * P.scale_log2;
+        need |= tmax[b] > mrow[b] + RESCALE_SLACK;
+      }
+      return __ballot(need) != 0ull;
+    };
+    auto set_use = [&]() {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) muse[b] = (mrow[b] == -INFINITY) ? 0.f : mrow[b];
+    };
+    // P = exp2(s c - m) for elements e, e + 1 of key block kb (e = 16 b + r),
+    // summed into l and written as bf16 into the P^T operand.
+    auto softmax2 = [&](int kb, int e) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int b = (e + x) >> 4, r = (e + x) & 15;
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][b][r], P.scale_log2, -muse[b]));
+        lrow[b] += pv;
+        pb[kb][r >> 3][b][r & 7] = (bf16)pv;
+      }
+    };
+
+    ldk(0);
+    ldk(1);
+    __builtin_amdgcn_sched_barrier(0);
+    // Stage A: scores of key block 0.
+#pragma unroll
+    for (int st = 0; st < NKS; ++st) {
+      ldk(st + 2);
+      s_step(st);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Stage B: scores of key block 1 under the softmax of block 0.  Its first
+    // step is issued before block 0's max is taken, so the matrix cores stay
+    // busy while the vector unit waits for block 0's last products.
+    ldk(NKS + 2);
+    s_step(NKS);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      float tmax[2];
+      if (block_max(0, tmax)) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const float mnew = fmaxf(mrow[b], tmax[b]);
+          const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrow[b] - mnew);
+          mrow[b] = mnew;
+          lrow[b] *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[db][b][r] *= alpha;
+        }
+      }
+      set_use();
+    }
+    constexpr int EB = 2 * ((NKS + 14) / (NKS - 1));  // block-0 softmax elements per remaining stage-B step (even)
+#pragma unroll
+    for (int st = NKS + 1; st < 2 * NKS; ++st) {
+      if (st + 2 < 2 * NKS) ldk(st + 2);
+      else ldv(st + 2 - 2 * NKS);
+      s_step(st);
+#pragma unroll
+      for (int e = (st - NKS - 1) * EB; e < (st - NKS) * EB && e < 32; e += 2) softmax2(0, e);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Stage C: O^T += V^T P^T for key block 0 under the softmax of block 1.
+    // Block 1's reference is settled first; the accumulator's rescale (which
+    // must include block 0's products) waits until they are in.
+    ldv(2);
+    pv_step(0);
+    __builtin_amdgcn_sched_barrier(0);
+    float alpha1[2] = {1.f, 1.f};
+    bool resc1;
+    {
+      float tmax[2];
+      resc1 = block_max(1, tmax);
+      if (resc1) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const float mnew = fmaxf(mrow[b], tmax[b]);
+          alpha1[b] = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrow[b] - mnew);
+          mrow[b] = mnew;
+          lrow[b] *= alpha1[b];
+        }
+      }
+      set_use();
+    }
+    constexpr int EC = 2 * ((2 * NDB + 14) / (2 * NDB - 1));  // block-1 softmax elements per remaining stage-C step
+#pragma unroll
+    for (int st = 1; st < 2 * NDB; ++st) {
+      ldv(st + 2);
+      pv_step(st);
+#pragma unroll
+      for (int e = (st - 1) * EC; e < st * EC && e < 32; e += 2) softmax2(1, e);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (resc1) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][b][r] *= alpha;
-      }
+          for (int r = 0; r < 16; ++r) acc[db][b][r] *= alpha1[b];
     }
+    // Stage D: O^T += V^T P^T for key block 1.
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const float muse = (mrow[b] == -INFINITY) ? 0.f : mrow[b];
-      float ls = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][b][r], P.scale_log2, -muse));
-          s[kb][b][r] = pv;
-          ls += pv;
-        }
-      lrow[b] += ls;
+    for (int st = 2 * NDB; st < 4 * NDB; ++st) {
+      if (st + 2 < 4 * NDB) ldv(st + 2);
+      pv_step(st);
+      __builtin_amdgcn_sched_barrier(0);
     }
-
-    __builtin_amdgcn_sched_barrier(0);
-    // 4. O^T += V^T P^T.
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        bf16x8 pb[2];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) pb[b] = to_bf16x8(s[kb][b], 8 * t2);
-        const int vrow = kb * 32 + 16 * t2 + 8 * hh + tr_row(lane);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int vcol = db * 32 + tr_col(lane);
-          const bf16x8 a = ld_tr8(Vs + vrow * VRS + vcol, Vs + (vrow + 4) * VRS + vcol);
-#pragma unroll
-          for (int b = 0; b < 2; ++b) acc[db][b] = mfma32(a, pb[b], acc[db][b]);
-        }
-      }
   }
 
   // Epilogue: O = O^T / l, LSE = (m + log2 l) ln 2.
