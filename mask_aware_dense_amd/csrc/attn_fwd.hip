@@ -25,9 +25,11 @@
 
 namespace mad {
 
-template <int D>
-__global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
-  constexpr int BM = BM0, BN = BN0, NKS = D / 16, NDB = D / 32;
+// NB: 32-row query blocks per wave (the workgroup's 128 rows are spread over
+// 4 / NB waves).
+template <int D, int NB>
+__global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
+  constexpr int BM = BM0, BN = BN0, NKS = D / 16, NDB = D / 32, NW = 4 / NB;
   constexpr int KRS = tile_rs<D, TILE_ROWS>(), KT = tile_elems<D, TILE_ROWS>();
   constexpr int VRS = tile_rs<D, TILE_TR>(), VT = tile_elems<D, TILE_TR>();
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * (KT + VT)];  // K0 V0 K1 V1
@@ -40,15 +42,15 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
   const int mg = h / P.grp_div;
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, li = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, wave-uniform
-  const int row_base = qt * BM + w * 64;
+  const int row_base = qt * BM + w * 32 * NB;
 
   const int32_t* ptr = P.t.ptr + (int64_t)mg * (P.t.nmajor + 1);
   const int beg = sld(ptr + qt), end = sld(ptr + qt + 1);
   const bf16* kg = P.k + (int64_t)g * P.k_head;
   const bf16* vg = P.v + (int64_t)g * P.v_head;
   const uint32_t smem_lds = lds_addr(smem);
-  TileLoader<D, TILE_ROWS, 2, true> kload;
-  TileLoader<D, TILE_TR, 2, false> vload;
+  TileLoader<D, TILE_ROWS, NW, true> kload;
+  TileLoader<D, TILE_TR, NW, false> vload;
   kload.init(P.k_tok, w, lane);
   vload.init(P.v_tok, w, lane);
   auto issue = [&](int kt, int buf) {
@@ -59,20 +61,20 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
   if (beg < end) issue(sld(P.t.ent + beg) & 0x7fffffff, 0);
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[row][16ks + 8hh .. +8].
-  bf16x8 qf[2][NKS];
+  bf16x8 qf[NB][NKS];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
+  for (int b = 0; b < NB; ++b) {
     const int row = row_base + b * 32 + li;
     const bf16* src = P.q + (int64_t)min(row, P.Tq - 1) * P.q_tok + (int64_t)h * P.q_head + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[b][ks] = ld16(src + 16 * ks);
   }
 
-  f32x16 acc[NDB][2];
+  f32x16 acc[NDB][NB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[db][b] = f32x16{};
+    for (int b = 0; b < NB; ++b) acc[db][b] = f32x16{};
   float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
 
   for (int it = beg; it < end; ++it) {
@@ -91,11 +93,11 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
     if (masked) {
       const int aux = partial ? sld(P.t.ent_aux + it) : -1;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
           mbits[b][kb] = keymask32(P.m, aux, mg, partial, row_base + b * 32 + li, kt * BN + kb * 32, row_base,
-                                   row_base + 63);
+                                   row_base + 32 * NB - 1);
       wait_vmem();
     }
     if (it + 1 < end) issue(sld(P.t.ent + it + 1) & 0x7fffffff, buf ^ 1);
@@ -106,17 +108,17 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
     // Scores start at 0, or at -inf on masked (row, key) pairs, so masking
     // costs nothing past this initialisation.  Register r of s[kb][b] holds
     // key kb*32 + 16(r/8) + 8hh + r%8 of row b*32 + li.
-    f32x16 s[2][2];
+    f32x16 s[2][NB];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) s[kb][b] = f32x16{};
+      for (int b = 0; b < NB; ++b) s[kb][b] = f32x16{};
     if (__builtin_expect(masked, 0)) {
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             if (!((mbits[b][kb] >> (16 * (r >> 3) + 8 * hh + (r & 7))) & 1u)) s[kb][b][r] = -INFINITY;
@@ -137,13 +139,13 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
     auto s_step = [&](int st) {  // S^T of key block st / NKS, k-step st % NKS, both query blocks
       const int kb = st / NKS, ks = st % NKS;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) s[kb][b] = mfma32(kr[st % 3], qf[b][ks], s[kb][b]);
+      for (int b = 0; b < NB; ++b) s[kb][b] = mfma32(kr[st % 3], qf[b][ks], s[kb][b]);
     };
-    bf16x8 pb[2][2][2];  // P^T operands [kb][t2][b]
+    bf16x8 pb[2][2][NB];  // P^T operands [kb][t2][b]
     auto pv_step = [&](int st) {  // O^T += V^T P^T for (kb, t2, db), both query blocks
       const int kb = st / (2 * NDB), t2 = (st / NDB) % 2, db = st % NDB;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) acc[db][b] = mfma32(vr[st % 3], pb[kb][t2][b], acc[db][b]);
+      for (int b = 0; b < NB; ++b) acc[db][b] = mfma32(vr[st % 3], pb[kb][t2][b], acc[db][b]);
     };
     // Online softmax in the exp2 domain against a lagging reference max per
     // row: p = exp2(s c - m_ref); m_ref moves (and O, l are rescaled by
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
     auto block_max = [&](int kb, float* tmax) {
       bool need = false;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+      for (int b = 0; b < NB; ++b) {
         float mx = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][b][r]);
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
     };
     auto set_use = [&]() {
 #pragma unroll
-      for (int b = 0; b < 2; ++b) muse[b] = (mrow[b] == -INFINITY) ? 0.f : mrow[b];
+      for (int b = 0; b < NB; ++b) muse[b] = (mrow[b] == -INFINITY) ? 0.f : mrow[b];
     };
     // P = exp2(s c - m) for elements e, e + 1 of key block kb (e = 16 b + r),
     // summed into l and written as bf16 into the P^T operand.
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
       float tmax[2];
       if (block_max(0, tmax)) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int b = 0; b < NB; ++b) {
           const float mnew = fmaxf(mrow[b], tmax[b]);
           const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrow[b] - mnew);
           mrow[b] = mnew;
@@ -213,14 +215,15 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
       }
       set_use();
     }
-    constexpr int EB = 2 * ((NKS + 14) / (NKS - 1));  // block-0 softmax elements per remaining stage-B step (even)
+    constexpr int NE = 16 * NB;  // softmax elements per key block and lane
+    constexpr int EB = 2 * ((NE / 2 + NKS - 2) / (NKS - 1));  // block-0 elements per remaining stage-B step (even)
 #pragma unroll
     for (int st = NKS + 1; st < 2 * NKS; ++st) {
       if (st + 2 < 2 * NKS) ldk(st + 2);
       else ldv(st + 2 - 2 * NKS);
       s_step(st);
 #pragma unroll
-      for (int e = (st - NKS - 1) * EB; e < (st - NKS) * EB && e < 32; e += 2) softmax2(0, e);
+      for (int e = (st - NKS - 1) * EB; e < (st - NKS) * EB && e < NE; e += 2) softmax2(0, e);
       __builtin_amdgcn_sched_barrier(0);
     }
     // Stage C: O^T += V^T P^T for key block 0 under the softmax of block 1.
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
       resc1 = block_max(1, tmax);
       if (resc1) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int b = 0; b < NB; ++b) {
           const float mnew = fmaxf(mrow[b], tmax[b]);
           alpha1[b] = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrow[b] - mnew);
           mrow[b] = mnew;
@@ -245,18 +248,18 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
       }
       set_use();
     }
-    constexpr int EC = 2 * ((2 * NDB + 14) / (2 * NDB - 1));  // block-1 softmax elements per remaining stage-C step
+    constexpr int EC = 2 * ((NE / 2 + 2 * NDB - 2) / (2 * NDB - 1));  // block-1 elements per remaining stage-C step
 #pragma unroll
     for (int st = 1; st < 2 * NDB; ++st) {
       ldv(st + 2);
       pv_step(st);
 #pragma unroll
-      for (int e = (st - 1) * EC; e < st * EC && e < 32; e += 2) softmax2(1, e);
+      for (int e = (st - 1) * EC; e < st * EC && e < NE; e += 2) softmax2(1, e);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (resc1) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -273,7 +276,7 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
 
   // Epilogue: O = O^T / l, LSE = (m + log2 l) ln 2.
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
+  for (int b = 0; b < NB; ++b) {
     const float lt = pair_sum(lrow[b]);
     const int row = row_base + b * 32 + li;
     if (row >= P.Tq) continue;
@@ -292,10 +295,12 @@ __global__ __launch_bounds__(128) void fwd_kernel(const AttnParams P) {
   }
 }
 
+constexpr int FWD_NB = 1;  // 4 waves of 32 rows: 220 registers, two waves per SIMD
+
 hipError_t launch_fwd(const AttnParams& P, int D, int n_items, hipStream_t stream) {
   if (n_items <= 0) return hipSuccess;
-  if (D == 128) hipLaunchKernelGGL(fwd_kernel<128>, dim3(n_items), dim3(128), 0, stream, P);
-  else hipLaunchKernelGGL(fwd_kernel<64>, dim3(n_items), dim3(128), 0, stream, P);
+  if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, FWD_NB>), dim3(n_items), dim3(256 / FWD_NB), 0, stream, P);
+  else hipLaunchKernelGGL((fwd_kernel<64, FWD_NB>), dim3(n_items), dim3(256 / FWD_NB), 0, stream, P);
   return hipGetLastError();
 }
 
