@@ -151,6 +151,9 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const AttnParams P) {
       wait_vmem();
     }
     if (it + 1 < end) issue(sld(P.t.ent + it + 1) & 0x7fffffff, buf ^ 1);
+    // A wave none of whose rows sees a key of this tile skips it; it only
+    // takes part in the loads and barriers.
+    if (masked && __ballot((mbits[0] | mbits[1]) != 0u) == 0ull) continue;
     const bf16* Ks = smem + buf * (KT + VT);
     const bf16* Vs = Ks + KT;
 

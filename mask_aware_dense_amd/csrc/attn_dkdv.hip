@@ -167,7 +167,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
     const float* nl_s = &rowv[buf][0];
     const float* nd_s = &rowv[buf][BM];
 
-    {
+    // A wave none of whose keys is seen by a row of this tile skips it; it
+    // only takes part in the loads and barriers.
+    if (!partial || __ballot((mw[0] | mw[1]) != 0u) != 0ull) {
       // Register r of block b holds query row b*32 + 8(r/4) + 4hh + r%4.  A
       // masked row starts its score at -inf, so its P (and dS) is exactly 0
       // after the products: the mask costs nothing past the initialisation.

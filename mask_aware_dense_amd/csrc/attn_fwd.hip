@@ -101,6 +101,15 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
       wait_vmem();
     }
     if (it + 1 < end) issue(sld(P.t.ent + it + 1) & 0x7fffffff, buf ^ 1);
+    if (masked) {
+      // A wave none of whose rows sees a key of this tile skips it (blocks
+      // smaller than the tile leave whole waves masked): it only takes part
+      // in the loads and barriers.
+      uint32_t any = 0u;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) any |= mbits[b][0] | mbits[b][1];
+      if (__ballot(any != 0u) == 0ull) continue;
+    }
     const bf16* Ks = smem + buf * (KT + VT);
     const bf16* Vs = Ks + KT;
     __builtin_amdgcn_sched_barrier(0);
