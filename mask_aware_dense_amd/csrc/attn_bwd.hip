@@ -136,14 +136,18 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const AttnParams P) {
     const uint32_t ent = (uint32_t)sld(P.t.ent + it);
     const int kt = (int)(ent & 0x7fffffffu);
     const bool partial = (ent & ENT_PARTIAL) != 0;
-    const bool masked = partial || (kt + 1) * BN > P.Tk;
+    // Block-sparse PARTIAL tiles whose wave strips are each FULL or EMPTY
+    // (FULL strips as bits in aux) run as FULL tiles on the FULL strips.
+    const bool ragged = (kt + 1) * BN > P.Tk;
+    const int aux = partial ? sld(P.t.ent_aux + it) : -1;
+    const bool parts = partial && !ragged && P.m.mode == MODE_BLOCKS && aux >= 0;
+    const bool masked = (partial && !parts) || ragged;
     wait_vmem();
     __syncthreads();
     // Allowed-key masks (PARTIAL and ragged tiles), evaluated before the next
     // tile's loads are issued so that the mask table reads never wait behind them.
     uint32_t mbits[2] = {0xffffffffu, 0xffffffffu};
     if (masked) {
-      const int aux = partial ? sld(P.t.ent_aux + it) : -1;
       const int r_lo = qt * BM + w * 32;  // the wave's rows, wave-uniform
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -153,6 +157,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const AttnParams P) {
     if (it + 1 < end) issue(sld(P.t.ent + it + 1) & 0x7fffffff, buf ^ 1);
     // A wave none of whose rows sees a key of this tile skips it; it only
     // takes part in the loads and barriers.
+    if (parts && !((aux >> w) & 1)) continue;
     if (masked && __ballot((mbits[0] | mbits[1]) != 0u) == 0ull) continue;
     const bf16* Ks = smem + buf * (KT + VT);
     const bf16* Vs = Ks + KT;

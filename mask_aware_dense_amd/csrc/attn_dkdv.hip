@@ -153,10 +153,16 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
     // Rows of the tile this lane's key may see (PARTIAL tiles), evaluated
     // before the next tiles' loads are issued so that the mask table reads
     // never wait behind them.
+    // Block-sparse PARTIAL tiles whose four key strips are each FULL or EMPTY
+    // carry the FULL strips as bits in aux: those waves run the item as a
+    // FULL one, the others skip it.
+    const int aux = partial ? sld(P.t.ent_aux + cur.it) : -1;
+    const bool parts = partial && P.m.mode == MODE_BLOCKS && aux >= 0;
+    const bool masked = partial && !parts;
     uint32_t mw[2] = {0u, 0u};
-    if (partial) {
+    if (masked) {
       const int k_lo = kt * BN + w * 32;  // the wave's keys, wave-uniform
-      const uint64_t rows = rowmask64(P.m, sld(P.t.ent_aux + cur.it), mg, key, q0, k_lo, k_lo + 31);
+      const uint64_t rows = rowmask64(P.m, aux, mg, key, q0, k_lo, k_lo + 31);
       mw[0] = (uint32_t)(rows >> (4 * hh));
       mw[1] = (uint32_t)(rows >> (32 + 4 * hh));
       wait_vmem();
@@ -169,7 +175,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
 
     // A wave none of whose keys is seen by a row of this tile skips it; it
     // only takes part in the loads and barriers.
-    if (!partial || __ballot((mw[0] | mw[1]) != 0u) != 0ull) {
+    if (parts ? ((aux >> w) & 1) != 0 : (!masked || __ballot((mw[0] | mw[1]) != 0u) != 0ull)) {
       // Register r of block b holds query row b*32 + 8(r/4) + 4hh + r%4.  A
       // masked row starts its score at -inf, so its P (and dS) is exactly 0
       // after the products: the mask costs nothing past the initialisation.
@@ -183,7 +189,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
           sc[b][4 * rg + 0] = l4.x; sc[b][4 * rg + 1] = l4.y; sc[b][4 * rg + 2] = l4.z; sc[b][4 * rg + 3] = l4.w;
           dp[b][4 * rg + 0] = d4.x; dp[b][4 * rg + 1] = d4.y; dp[b][4 * rg + 2] = d4.z; dp[b][4 * rg + 3] = d4.w;
         }
-        if (partial) {
+        if (masked) {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             if (!((mw[b] >> (8 * (r >> 2) + (r & 3))) & 1u)) sc[b][r] = -INFINITY;

@@ -88,10 +88,15 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
     // Allowed-key masks of this lane's two rows (PARTIAL and ragged tiles
     // only), evaluated before the next tile's loads are issued so that the
     // mask table reads never wait behind them.
-    const bool masked = partial || (kt + 1) * BN > P.Tk;
+    // A block-sparse PARTIAL tile whose four wave strips are each FULL or
+    // EMPTY carries the FULL strips as bits in aux: those waves run it as a
+    // FULL tile and the others skip it, with no mask arithmetic.
+    const bool ragged = (kt + 1) * BN > P.Tk;
+    const int aux = partial ? sld(P.t.ent_aux + it) : -1;
+    const bool parts = partial && !ragged && P.m.mode == MODE_BLOCKS && aux >= 0;
+    const bool masked = (partial && !parts) || ragged;
     uint32_t mbits[2][2];
     if (masked) {
-      const int aux = partial ? sld(P.t.ent_aux + it) : -1;
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -101,6 +106,7 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
       wait_vmem();
     }
     if (it + 1 < end) issue(sld(P.t.ent + it + 1) & 0x7fffffff, buf ^ 1);
+    if (parts && !((aux >> w) & 1)) continue;
     if (masked) {
       // A wave none of whose rows sees a key of this tile skips it (blocks
       // smaller than the tile leave whole waves masked): it only takes part

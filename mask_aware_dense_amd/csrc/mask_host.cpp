@@ -168,9 +168,51 @@ static bool keep_bit(const mad_plan* p, int g, int qb, int kb) {
   return (p->keep[((size_t)g * p->n_qb + qb) * p->nw + (kb >> 6)] >> (kb & 63)) & 1u;
 }
 
+// Class of the block-mask rectangle rows [r0, r1) x keys [c0, c1) (in range,
+// non-empty) for group g.
+static uint8_t rect_class(const mad_plan* p, int g, int64_t r0, int64_t r1, int64_t c0, int64_t c1) {
+  const int qa = p->row_qb[r0], qz = p->row_qb[r1 - 1];
+  const int ka = p->col_kb[c0], kz = p->col_kb[c1 - 1];
+  bool any = false, all = true;
+  for (int qb = qa; qb <= qz; ++qb)
+    for (int kb = ka; kb <= kz; ++kb) {
+      const bool k = keep_bit(p, g, qb, kb);
+      any |= k;
+      all &= k;
+    }
+  return !any ? CLS_EMPTY : (all ? CLS_FULL : CLS_PARTIAL);
+}
+
+// A PARTIAL tile is also split into the four parts its kernel hands to its
+// four waves (tiling 0: 32-row strips; tiling 1: 32-key strips).  When every
+// part is FULL or EMPTY -- blocks aligned to the strips, e.g. 64- or 128-token
+// blocks -- the tile's aux entry records which parts are FULL (bit w for wave
+// w), and each wave then runs its part without mask arithmetic or skips it;
+// otherwise aux stays -1 and the waves evaluate the keep bitmap.
+static int32_t wave_parts(const mad_plan* p, int g, bool rows_split, int64_t r0, int64_t r1, int64_t c0,
+                          int64_t c1) {
+  int32_t full = 0;
+  for (int w = 0; w < 4; ++w) {
+    int64_t a0 = r0, a1 = r1, b0 = c0, b1 = c1;
+    if (rows_split) {
+      a0 = r0 + 32 * w;
+      a1 = std::min<int64_t>(r1, a0 + 32);
+    } else {
+      b0 = c0 + 32 * w;
+      b1 = std::min<int64_t>(c1, b0 + 32);
+    }
+    if (a0 >= a1 || b0 >= b1) continue;  // nothing in range: EMPTY
+    const uint8_t c = rect_class(p, g, a0, a1, b0, b1);
+    if (c == CLS_PARTIAL) return -1;
+    if (c == CLS_FULL) full |= 1 << w;
+  }
+  return full;
+}
+
 static void classify_blocks(mad_plan* p, TilingHost& t) {
   const int BM = t.BM, BN = t.BN;
   const int64_t Tq = p->Tq, Tk = p->Tk;
+  const bool rows_split = BM == BM0;  // tiling 0 gives each wave 32 rows; tiling 1 gives each 32 keys
   t.nqt = (int)((Tq + BM - 1) / BM);
   t.nkt = (int)((Tk + BN - 1) / BN);
   const int64_t ntiles = (int64_t)t.nqt * t.nkt;
@@ -178,21 +220,16 @@ static void classify_blocks(mad_plan* p, TilingHost& t) {
   t.aux.assign(p->G, std::vector<int32_t>());
   auto work = [&](int g) {
     auto& cls = t.cls[g];
+    auto& aux = t.aux[g];
     cls.assign(ntiles, CLS_EMPTY);
+    aux.assign(ntiles, -1);
     for (int qt = 0; qt < t.nqt; ++qt) {
       const int64_t r0 = (int64_t)qt * BM, r1 = std::min<int64_t>(Tq, r0 + BM);
-      const int qa = p->row_qb[r0], qz = p->row_qb[r1 - 1];
       for (int kt = 0; kt < t.nkt; ++kt) {
         const int64_t c0 = (int64_t)kt * BN, c1 = std::min<int64_t>(Tk, c0 + BN);
-        const int ka = p->col_kb[c0], kz = p->col_kb[c1 - 1];
-        bool any = false, all = true;
-        for (int qb = qa; qb <= qz; ++qb)
-          for (int kb = ka; kb <= kz; ++kb) {
-            bool k = keep_bit(p, g, qb, kb);
-            any |= k;
-            all &= k;
-          }
-        cls[(int64_t)qt * t.nkt + kt] = !any ? CLS_EMPTY : (all ? CLS_FULL : CLS_PARTIAL);
+        const uint8_t c = rect_class(p, g, r0, r1, c0, c1);
+        cls[(int64_t)qt * t.nkt + kt] = c;
+        if (c == CLS_PARTIAL) aux[(int64_t)qt * t.nkt + kt] = wave_parts(p, g, rows_split, r0, r1, c0, c1);
       }
     }
   };
