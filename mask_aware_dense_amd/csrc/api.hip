@@ -3,6 +3,7 @@
 // Every entry point validates all arguments before it launches or writes
 // anything, returns a mad_status, and records a message for mad_last_error()
 // on the calling thread.  Kernels run on the caller's stream.
+#include <algorithm>
 #include <cstring>
 #include <string>
 
@@ -62,6 +63,32 @@ mad_status check_common(const char* fn, const mad_plan* p, const void* q, const 
   if (Tq > 0 && Tk > 0 && (!q || !k || !v)) return fail(MAD_ERR_INVALID, f + ": q/k/v must not be NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return fail(MAD_ERR_UNSUPPORTED, f + ": q/k/v must be 16-byte aligned");
   return MAD_OK;
+}
+
+// Workgroups per key-tile column of the dK/dV kernel.  The kernel runs one
+// workgroup per CU (256 CUs); when its longest column holds more than half of
+// one CU's average share of the items, that column alone would set the
+// kernel's length, so every column is cut into S chunks with the longest
+// chunk at most that half-share (S capped at 8).  Balanced masks keep S = 1
+// (CAUSAL 32K GQA: the longest column is a quarter of the average share).
+int dkdv_splits(const mad_plan* p, int32_t Hq, int32_t Hkv) {
+  const TilingHost& t = p->tiling[1];
+  const int R = Hq / Hkv, grp_div = Hq / p->G, nk = t.nkt;
+  if (nk == 0 || t.ptr.empty()) return 1;
+  int64_t total = 0, mx = 0;
+  for (int g = 0; g < Hkv; ++g)
+    for (int kt = 0; kt < nk; ++kt) {
+      int64_t n = 0;
+      for (int e = 0; e < R; ++e) {
+        const int mg = (g * R + e) / grp_div;
+        n += t.ptr[(size_t)mg * (nk + 1) + kt + 1] - t.ptr[(size_t)mg * (nk + 1) + kt];
+      }
+      total += n;
+      mx = std::max(mx, n);
+    }
+  if (total == 0) return 1;
+  constexpr int64_t kCUs = 256;
+  return (int)std::min<int64_t>(8, std::max<int64_t>(1, (mx * 2 * kCUs + total - 1) / total));
 }
 
 AttnParams base_params(const mad_plan* p, int which, const void* q, const void* k, const void* v, int32_t Tq,
@@ -233,9 +260,11 @@ extern "C" mad_status mad_bwd_workspace_bytes(const mad_plan* p, int32_t Tq, int
   if (!p) return fail(MAD_ERR_INVALID, "mad_bwd_workspace_bytes: plan is NULL");
   if (Tq < 0 || Tk < 0 || Hq <= 0 || Hkv <= 0) return fail(MAD_ERR_INVALID, "mad_bwd_workspace_bytes: bad sizes");
   if (d != 64 && d != 128) return fail(MAD_ERR_UNSUPPORTED, "mad_bwd_workspace_bytes: head dim must be 64 or 128");
-  // -delta and -LSE/scale rows, each [Hq][Tq rounded up to 128] fp32
+  // -delta and -LSE/scale rows, each [Hq][Tq rounded up to 128] fp32; with
+  // split dK/dV columns, fp32 dK and dV sums [Tk][Hkv][d] after them
   const size_t tq_pad = ((size_t)Tq + 127) / 128 * 128;
-  *bytes = 2 * (size_t)Hq * tq_pad * 4;
+  *bytes = (2 * (size_t)Hq * tq_pad * 4 + 255) / 256 * 256;
+  if (Hq % Hkv == 0 && Hq % p->G == 0 && dkdv_splits(p, Hq, Hkv) > 1) *bytes += 2 * (size_t)Tk * Hkv * d * 4;
   return MAD_OK;
 }
 
@@ -276,6 +305,13 @@ mad_status attn_bwd_impl(const mad_plan* p, const void* q, const void* k, const 
   Pq.dv = (bf16*)dv;
   AttnParams Pkv = Pq;
   Pkv.t = p->tdev[1];
+  Pkv.kv_splits = dkdv_splits(p, Hq, Hkv);
+  if (Pkv.kv_splits > 1) {
+    char* acc = (char*)workspace + (2 * (size_t)Hq * Pq.Tq_pad * 4 + 255) / 256 * 256;
+    Pkv.dk_acc = (float*)acc;
+    Pkv.dv_acc = (float*)acc + (size_t)Tk * Hkv * d;
+  }
+  Pq.kv_splits = 1;
   const int64_t nq = Tq > 0 ? (int64_t)p->tiling[0].nqt * Hq : 0;
   const int64_t nkv = Tk > 0 ? (int64_t)p->tiling[1].nkt * Hkv : 0;
   if (nq > INT32_MAX || nkv > INT32_MAX) return fail(MAD_ERR_UNSUPPORTED, "mad_attn_bwd: too many work items");

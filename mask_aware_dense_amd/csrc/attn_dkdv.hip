@@ -24,6 +24,8 @@
 // dP holds dO.v - D when the products finish.  LDS operands are read two
 // MFMA steps ahead of their use through a three-slot register ring; every
 // step ends in a scheduling fence so that the compiler keeps that distance.
+#include <algorithm>
+
 #include "kernel_common.hpp"
 
 namespace mad {
@@ -39,9 +41,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
   __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];   // Q0 dO0 Q1 dO1
   __shared__ __attribute__((aligned(256))) float rowv[2][2 * BM];  // per buffer: -LSE/scale[64], -D[64]
 
-  const int L = blockIdx.x;
-  const int kt = sld(P.t.order + L / P.Hkv);
-  const int g = L % P.Hkv;
+  // Workgroup -> (KV head g, key tile kt of the longest-first order, chunk
+  // seg of that column's items).  Consecutive workgroups share g's XCD.
+  const int L = blockIdx.x, S = P.kv_splits;
+  const int g = L % P.Hkv, rest = L / P.Hkv;
+  const int kt = sld(P.t.order + rest / S), seg = rest % S;
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, li = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, wave-uniform
   const int key = kt * BN + w * 32 + li;
@@ -75,8 +79,13 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
   // workgroups running together read the same Q / dO tiles and share them in
   // L2 (walking up from each key tile's first tile would spread them apart).
   // Otherwise each head's list is walked in turn.
+  // With kv_splits = S > 1 the column's items are cut into S contiguous
+  // chunks, one per workgroup (a few very long columns -- key tiles every
+  // query sees, as under GLOBAL_SLIDING -- would otherwise set the kernel's
+  // length on their own); the chunks' partial dK / dV are summed in fp32.
   struct Cursor {
     int e, it, end;  // shared list: `it` runs down to `end` (the list start)
+    int left;        // items of this workgroup's chunk still to visit
     bool ok;
   };
   const int h0 = g * P.R;
@@ -89,22 +98,54 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
   };
   auto settle = [&](Cursor& cu) {  // move past exhausted heads
     while (cu.it >= cu.end && cu.e + 1 < P.R) head_list(cu.e + 1, cu);
-    cu.ok = cu.it < cu.end;
   };
+  int n0 = 0, n1 = 0;  // this workgroup's chunk of the column's items
   auto first = [&]() {
     Cursor cu;
     head_list(0, cu);
+    int ncol;
+    if (shared) {
+      ncol = P.R * (cu.end - cu.it);
+    } else {
+      ncol = 0;
+      for (int e = 0; e < P.R; ++e) {
+        Cursor x;
+        head_list(e, x);
+        ncol += x.end - x.it;
+      }
+    }
+    n0 = (int)((int64_t)seg * ncol / S);
+    n1 = (int)((int64_t)(seg + 1) * ncol / S);
+    cu.left = n1 - n0;
     if (shared) {
       const int list_begin = cu.it;
-      cu.it = cu.end - 1;
+      cu.e = n0 % P.R;
+      cu.it = cu.end - 1 - n0 / P.R;
       cu.end = list_begin;
-      cu.ok = cu.it >= cu.end;
     } else {
+      int skip = n0;
       settle(cu);
+      while (skip > 0) {
+        const int len = cu.end - cu.it;
+        if (len <= 0) break;  // lists exhausted (not reached: n0 < the column's item count)
+        if (skip < len) {
+          cu.it += skip;
+          skip = 0;
+        } else {
+          skip -= len;
+          cu.it = cu.end;
+          settle(cu);
+        }
+      }
     }
+    cu.ok = cu.left > 0 && (shared || cu.it < cu.end);
     return cu;
   };
   auto advance = [&](Cursor cu) {
+    if (--cu.left <= 0) {
+      cu.ok = false;
+      return cu;
+    }
     if (shared) {
       if (cu.e + 1 < P.R) {
         ++cu.e;
@@ -112,10 +153,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
         cu.e = 0;
         --cu.it;
       }
-      cu.ok = cu.it >= cu.end;
+      cu.ok = true;
     } else {
       ++cu.it;
       settle(cu);
+      cu.ok = cu.it < cu.end;
     }
     return cu;
   };
@@ -266,6 +308,22 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
   }
 
   // dK, dV: lane holds column d = db*32 + li of key rows 8(r/4) + 4hh + r%4 of the wave's 32 keys.
+  if (S > 1) {
+    if (n1 > n0) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = kt * BN + w * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (kk < P.Tk) {
+            const int64_t off = ((int64_t)kk * P.Hkv + g) * D + db * 32 + li;
+            unsafeAtomicAdd(P.dk_acc + off, dka[db][r] * P.scale);
+            unsafeAtomicAdd(P.dv_acc + off, dva[db][r]);
+          }
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -279,9 +337,33 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
     }
 }
 
+// Column chunks: zero the fp32 sums before, round them to bf16 after.
+__global__ __launch_bounds__(256) void zero2_kernel(float* a, float* b, int64_t n4) {
+  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n4; x += (int64_t)gridDim.x * 256) {
+    reinterpret_cast<float4*>(a)[x] = float4{0.f, 0.f, 0.f, 0.f};
+    reinterpret_cast<float4*>(b)[x] = float4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+__global__ __launch_bounds__(256) void round2_kernel(const float* a, const float* b, bf16* ra, bf16* rb, int64_t n4) {
+  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n4; x += (int64_t)gridDim.x * 256) {
+    const float4 u = reinterpret_cast<const float4*>(a)[x], v = reinterpret_cast<const float4*>(b)[x];
+    bf16x4 y, z;
+    y[0] = (bf16)u.x; y[1] = (bf16)u.y; y[2] = (bf16)u.z; y[3] = (bf16)u.w;
+    z[0] = (bf16)v.x; z[1] = (bf16)v.y; z[2] = (bf16)v.z; z[3] = (bf16)v.w;
+    reinterpret_cast<bf16x4*>(ra)[x] = y;
+    reinterpret_cast<bf16x4*>(rb)[x] = z;
+  }
+}
+
 hipError_t launch_dkdv(const AttnParams& P, int D, int n_items, hipStream_t stream) {
-  if (D == 128) hipLaunchKernelGGL(dkdv_kernel<128>, dim3(n_items), dim3(256), 0, stream, P);
-  else hipLaunchKernelGGL(dkdv_kernel<64>, dim3(n_items), dim3(256), 0, stream, P);
+  const int S = P.kv_splits;
+  const int64_t n4 = (int64_t)P.Tk * P.Hkv * D / 4;  // D is a multiple of 4
+  const int nb = (int)std::min<int64_t>((n4 + 255) / 256, 4096);
+  if (S > 1 && n4 > 0) hipLaunchKernelGGL(zero2_kernel, dim3(nb), dim3(256), 0, stream, P.dk_acc, P.dv_acc, n4);
+  if (D == 128) hipLaunchKernelGGL(dkdv_kernel<128>, dim3(n_items * S), dim3(256), 0, stream, P);
+  else hipLaunchKernelGGL(dkdv_kernel<64>, dim3(n_items * S), dim3(256), 0, stream, P);
+  if (S > 1 && n4 > 0)
+    hipLaunchKernelGGL(round2_kernel, dim3(nb), dim3(256), 0, stream, P.dk_acc, P.dv_acc, P.dk, P.dv, n4);
   return hipGetLastError();
 }
 

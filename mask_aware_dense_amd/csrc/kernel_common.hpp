@@ -46,6 +46,9 @@ struct AttnParams {
   float* dq_acc;      // backward: if set, dQ is added into this fp32 [Tq, Hq, D] buffer instead of written to dq
   bf16* dk;
   bf16* dv;
+  float* dk_acc;      // dK/dV kernel with kv_splits > 1: fp32 [Tk, Hkv, D] sums of the column chunks
+  float* dv_acc;
+  int32_t kv_splits;  // dK/dV kernel: workgroups per key-tile column (1: each column in one workgroup)
   int64_t q_tok, q_head, k_tok, k_head, v_tok, v_head;
   int32_t Tq, Tk, Hq, Hkv;
   int32_t R;        // Hq / Hkv

@@ -284,8 +284,12 @@ extern "C" mad_status mad_ring_create(int32_t layout, int32_t n_ranks, int32_t c
   // Device buffers, one allocation.
   const int64_t S = (int64_t)r->steps.size();
   const int64_t qe = (int64_t)chunk * Hq * d;
-  size_t ws = 0;
-  if (S > 0) mad_bwd_workspace_bytes(r->steps[0].plan, chunk, chunk, Hq, Hkv, d, &ws);
+  size_t ws = 0;  // the largest workspace any step's backward needs
+  for (const auto& st : r->steps) {
+    size_t w = 0;
+    mad_bwd_workspace_bytes(st.plan, chunk, chunk, Hq, Hkv, d, &w);
+    ws = std::max(ws, w);
+  }
   size_t total = 0;
   auto take = [&](size_t b) {
     const size_t off = total;
