@@ -206,17 +206,22 @@ mad_status mad_attn_fwd(const mad_plan* plan, const void* q, const void* k, cons
                         int32_t d, const int64_t* strides, float scale, hipStream_t stream);
 
 /* Bytes of device workspace mad_attn_bwd needs: two fp32 [Hq][Tq rounded up
- * to 128] arrays, the delta rows D = rowsum(dO * O) and LSE * log2(e) (+inf
- * for rows with no allowed key and for padding rows). */
+ * to 128] arrays holding -D (D = rowsum(dO * O)) and -LSE / scale per row
+ * (-inf for rows with no allowed key and for padding rows), and, when the
+ * plan's key-tile columns are uneven enough that the dK/dV kernel cuts the
+ * longest ones between several workgroups, two fp32 [Tk][Hkv][d] sums for
+ * dK and dV.  Depends on the plan, so query it per plan. */
 mad_status mad_bwd_workspace_bytes(const mad_plan* plan, int32_t Tq, int32_t Tk, int32_t Hq,
                                    int32_t Hkv, int32_t d, size_t* bytes);
 
 /* Backward of the forward above for upstream gradient d_o, given o and lse
  * (normally the forward's; for a ring step the merged global ones, so the
  * step's share of the global gradient is produced).  Runs the delta pre-pass
- * D = rowsum(d_o * o) (and LSE * log2 e) into the workspace, then the dK/dV
+ * D = rowsum(d_o * o) (and LSE / scale) into the workspace, then the dK/dV
  * kernel and the dQ kernel.  dq, dk, dv are overwritten.  workspace must be 256-byte aligned
- * and at least mad_bwd_workspace_bytes long; q/k/v/o/d_o are not modified. */
+ * and at least mad_bwd_workspace_bytes long; q/k/v/o/d_o are not modified.
+ * Results are bit-reproducible, except dk/dv of plans whose columns are cut
+ * (their fp32 partial sums are added in arrival order). */
 mad_status mad_attn_bwd(const mad_plan* plan, const void* q, const void* k, const void* v,
                         const void* o, const void* d_o, const float* lse, void* dq, void* dk,
                         void* dv, void* workspace, size_t workspace_bytes, int32_t Tq,
