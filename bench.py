@@ -213,8 +213,28 @@ def suite_workloads(seed):
         ("PREFIX_LM", {}), ("SHARED_QUESTION", {"question": 2048, "n_answers": 4}),
         ("GLOBAL_SLIDING", {"global_len": 256, "window": 2048}), ("CAUSAL_BLOCKWISE", {"block": 2048}),
         ("BLOCK_CAUSAL_DOCUMENT", {"block": 1024, "doc_lens": docs}), ("PREFIX_LM_DOCUMENT", {"doc_lens": docs}),
+        ("CAUSAL_BLOCKWISE_LAST", {"block": 2048}),
+        ("BLOCK_CAUSAL_DOCUMENT_GLOBAL", {"block": 1024, "doc_lens": docs}),
     ]:
         out.append((f"{pattern} 32K GQA 64:8", static(pattern, **kw)))
+
+    def varlen_continuation():
+        # a batch of the same 32K of documents as keys; each sequence's queries are the
+        # last half of its tokens (a chunk that continues a cached prefix), causal,
+        # bottom-right aligned
+        def build(mad):
+            lk = np.asarray(docs, dtype=np.int64)
+            lq = lk - lk // 2
+            cq = np.concatenate([[0], np.cumsum(lq)])
+            ck = np.concatenate([[0], np.cumsum(lk)])
+            sl = mad.varlen_slices(cq, ck, causal=True, bottom_right=True)
+            Tq, Tk = int(cq[-1]), int(ck[-1])
+            return mad.mask_compile(sl, Tq, Tk), Tq, Tk, 64, 8, 128, {
+                "mask": "VARLEN causal bottom-right", "seq_len_q": Tq, "seq_len_k": Tk,
+                "batch": len(docs), "queries": "last half of each sequence"}
+        return build
+
+    out.append(("VARLEN continuation 32K keys GQA 64:8", varlen_continuation()))
 
     def sparse(S, Hq, Hkv, b, pct, variable):
         def build(mad):

@@ -90,7 +90,15 @@ typedef enum {
   MAD_MASK_GLOBAL_SLIDING = 8,                 /* j <= i and (j < G or i - j < W) */
   MAD_MASK_CAUSAL_BLOCKWISE = 9,               /* causal in a block, full to earlier blocks */
   MAD_MASK_BLOCK_CAUSAL_DOCUMENT = 10,         /* same document, block-causal from the doc start */
-  MAD_MASK_PREFIX_LM_DOCUMENT = 11             /* prefix LM inside each document, p = L/4 */
+  MAD_MASK_PREFIX_LM_DOCUMENT = 11,            /* prefix LM inside each document, p = L/4 */
+  /* Alternative readings of two heterogeneous patterns (the pages name them
+   * without a formula; the readings above are the ones the workloads use):   */
+  MAD_MASK_CAUSAL_BLOCKWISE_LAST = 12,         /* causal inside each block of B; only the last
+                                                  block also sees every earlier block in full
+                                                  (the in-context-learning layout: independent
+                                                  demonstrations, one query block over all) */
+  MAD_MASK_BLOCK_CAUSAL_DOCUMENT_GLOBAL = 13   /* same document and floor(j/B) <= floor(i/B):
+                                                  block edges at multiples of B from token 0 */
 } mad_mask_pattern;
 
 typedef struct {
@@ -99,7 +107,7 @@ typedef struct {
   int32_t question;        /* SHARED_QUESTION: question length */
   int32_t n_answers;       /* SHARED_QUESTION: answers split the rest equally, the last takes the remainder */
   int32_t global_len;      /* GLOBAL_SLIDING: G */
-  int32_t block;           /* CAUSAL_BLOCKWISE and BLOCK_CAUSAL_DOCUMENT block size (> 0) */
+  int32_t block;           /* CAUSAL_BLOCKWISE*, BLOCK_CAUSAL_DOCUMENT* block size (> 0) */
   const int32_t* doc_lens; /* *_DOCUMENT: host array of n_docs lengths summing to T */
   int32_t n_docs;
 } mad_mask_params;
@@ -109,6 +117,24 @@ typedef struct {
  * *n_out receives the number of slices.  Host only; launches nothing. */
 mad_status mad_mask_slices(int32_t pattern, int32_t T, const mad_mask_params* params,
                            mad_slice* out, int64_t cap, int64_t* n_out);
+
+/* Slices of a batch of packed variable-length sequences (the varlen layout
+ * of LongCA-bench section 2.1.1: sequences of different lengths packed into
+ * one token stream), given cumulative offsets cu_q[0..batch] and
+ * cu_k[0..batch] (cu_q[0] = cu_k[0] = 0, non-decreasing): query tokens
+ * [cu_q[b], cu_q[b+1]) attend keys [cu_k[b], cu_k[b+1]) of the same
+ * sequence only.  causal = 0: every key of the sequence.  causal = 1: with
+ * local offsets r = i - cu_q[b], c = j - cu_k[b] and lengths Lq, Lk, the key
+ * is allowed when c <= r (bottom_right = 0, top-left alignment, the slices'
+ * own convention) or c <= r + Lk - Lq (bottom_right = 1: the last query sees
+ * the last key, the usual convention for a query chunk that continues a
+ * longer key stream).  window W > 0 (causal only) further requires
+ * r - c < W (top-left) or r + Lk - Lq - c < W (bottom-right; rejected when
+ * some sequence has Lk > Lq, a shape the slice vocabulary cannot express).
+ * Tq = cu_q[batch], Tk = cu_k[batch] are the sizes to compile with.
+ * out / cap / n_out as in mad_mask_slices.  Host only. */
+mad_status mad_varlen_slices(const int32_t* cu_q, const int32_t* cu_k, int32_t batch, int32_t causal,
+                             int32_t window, int32_t bottom_right, mad_slice* out, int64_t cap, int64_t* n_out);
 
 /* One GPU's share of a context-parallel ring step (LongCA-bench section 2.3
  * and the notes' key design 3).  The causal sequence of n_ranks * chunk tokens

@@ -15,7 +15,7 @@ import os
 import numpy as np
 
 __all__ = [
-    "MadError", "lib", "Plan", "mask_slices", "ring_step_slices", "block_topk",
+    "MadError", "lib", "Plan", "mask_slices", "ring_step_slices", "varlen_slices", "block_topk",
     "mask_compile", "sparse_plan", "attn_fwd", "attn_bwd", "attn_bwd_phases", "bwd_workspace_bytes",
     "block_mask", "block_mask_workspace_bytes", "lse_merge", "Ring", "BWD_DELTA", "BWD_DKDV", "BWD_DQ", "BWD_ALL",
     "PATTERNS", "SLICE_DTYPE",
@@ -28,7 +28,7 @@ PATTERNS = {
     "FULL": 0, "CAUSAL": 1, "SLIDING_WINDOW": 2, "FULL_DOCUMENT": 3, "CAUSAL_DOCUMENT": 4,
     "SLIDING_WINDOW_CAUSAL_DOCUMENT": 5, "PREFIX_LM": 6, "SHARED_QUESTION": 7,
     "GLOBAL_SLIDING": 8, "CAUSAL_BLOCKWISE": 9, "BLOCK_CAUSAL_DOCUMENT": 10,
-    "PREFIX_LM_DOCUMENT": 11,
+    "PREFIX_LM_DOCUMENT": 11, "CAUSAL_BLOCKWISE_LAST": 12, "BLOCK_CAUSAL_DOCUMENT_GLOBAL": 13,
 }
 
 BWD_DELTA, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
@@ -61,6 +61,7 @@ _PI32 = ctypes.POINTER(ctypes.c_int32)
 _SIGS = {
     "mad_mask_slices": (_I32, [_I32, _I32, ctypes.POINTER(_Params), _VP, _I64, _PI64]),
     "mad_ring_step_slices": (_I32, [_I32, _I32, _I32, _I32, _I32, _VP, _I64, _PI64]),
+    "mad_varlen_slices": (_I32, [_VP, _VP, _I32, _I32, _I32, _I32, _VP, _I64, _PI64]),
     "mad_block_topk": (_I32, [_VP, _I32, _I32, _I32, _I32, _VP]),
     "mad_mask_compile": (_I32, [_VP, _I64, _I32, _I32, ctypes.POINTER(_VP)]),
     "mad_sparse_plan": (_I32, [_I32, _VP, _I32, _VP, _I32, _VP, ctypes.POINTER(_VP)]),
@@ -145,6 +146,23 @@ def mask_slices(pattern, T: int, window: int = 4096, prefix: int = -1, question:
     out = np.zeros(n.value, dtype=SLICE_DTYPE)
     _check(lib().mad_mask_slices(pid, T, ctypes.byref(prm), out.ctypes.data if n.value else None,
                                  n.value, ctypes.byref(n)))
+    return out
+
+
+def varlen_slices(cu_q, cu_k=None, causal: bool = True, window: int = 0, bottom_right: bool = False) -> np.ndarray:
+    """Slices of a batch of packed variable-length sequences from cumulative offsets (cu_seqlens).
+
+    cu_k defaults to cu_q (self-attention).  Compile with Tq = cu_q[-1], Tk = cu_k[-1]."""
+    cq = np.ascontiguousarray(np.asarray(cu_q, dtype=np.int32))
+    ck = cq if cu_k is None else np.ascontiguousarray(np.asarray(cu_k, dtype=np.int32))
+    if cq.ndim != 1 or ck.shape != cq.shape or cq.size == 0:
+        raise ValueError("cu_q and cu_k must be 1-D with the same length >= 1")
+    batch = cq.size - 1
+    n = ctypes.c_int64(0)
+    args = (cq.ctypes.data, ck.ctypes.data, batch, int(bool(causal)), int(window), int(bool(bottom_right)))
+    _check(lib().mad_varlen_slices(*args, None, 0, ctypes.byref(n)))
+    out = np.zeros(n.value, dtype=SLICE_DTYPE)
+    _check(lib().mad_varlen_slices(*args, out.ctypes.data if n.value else None, n.value, ctypes.byref(n)))
     return out
 
 

@@ -339,7 +339,8 @@ extern "C" mad_status mad_mask_slices(int32_t pattern, int32_t T, const mad_mask
   const mad_mask_params& P = prm ? *prm : d;
   const bool doc = pattern == MAD_MASK_FULL_DOCUMENT || pattern == MAD_MASK_CAUSAL_DOCUMENT ||
                    pattern == MAD_MASK_SLIDING_WINDOW_CAUSAL_DOCUMENT ||
-                   pattern == MAD_MASK_BLOCK_CAUSAL_DOCUMENT || pattern == MAD_MASK_PREFIX_LM_DOCUMENT;
+                   pattern == MAD_MASK_BLOCK_CAUSAL_DOCUMENT || pattern == MAD_MASK_PREFIX_LM_DOCUMENT ||
+                   pattern == MAD_MASK_BLOCK_CAUSAL_DOCUMENT_GLOBAL;
   if (doc) {
     if (!P.doc_lens || P.n_docs < 0) return fail(MAD_ERR_INVALID, "mad_mask_slices: document pattern needs doc_lens");
     int64_t sum = 0;
@@ -352,7 +353,9 @@ extern "C" mad_status mad_mask_slices(int32_t pattern, int32_t T, const mad_mask
   const bool windowed = pattern == MAD_MASK_SLIDING_WINDOW || pattern == MAD_MASK_SLIDING_WINDOW_CAUSAL_DOCUMENT ||
                         pattern == MAD_MASK_GLOBAL_SLIDING;
   if (windowed && P.window <= 0) return fail(MAD_ERR_INVALID, "mad_mask_slices: window must be > 0");
-  if ((pattern == MAD_MASK_CAUSAL_BLOCKWISE || pattern == MAD_MASK_BLOCK_CAUSAL_DOCUMENT) && P.block <= 0)
+  const bool blocked = pattern == MAD_MASK_CAUSAL_BLOCKWISE || pattern == MAD_MASK_BLOCK_CAUSAL_DOCUMENT ||
+                       pattern == MAD_MASK_CAUSAL_BLOCKWISE_LAST || pattern == MAD_MASK_BLOCK_CAUSAL_DOCUMENT_GLOBAL;
+  if (blocked && P.block <= 0)
     return fail(MAD_ERR_INVALID, "mad_mask_slices: block must be > 0");
   if (pattern == MAD_MASK_SHARED_QUESTION && (P.question < 0 || P.n_answers <= 0))
     return fail(MAD_ERR_INVALID, "mad_mask_slices: question >= 0 and n_answers > 0 required");
@@ -369,6 +372,7 @@ extern "C" mad_status mad_mask_slices(int32_t pattern, int32_t T, const mad_mask
     case MAD_MASK_CAUSAL_DOCUMENT:
     case MAD_MASK_SLIDING_WINDOW_CAUSAL_DOCUMENT:
     case MAD_MASK_BLOCK_CAUSAL_DOCUMENT:
+    case MAD_MASK_BLOCK_CAUSAL_DOCUMENT_GLOBAL:
     case MAD_MASK_PREFIX_LM_DOCUMENT: {
       int32_t s0 = 0;
       for (int32_t x = 0; x < P.n_docs; ++x) {
@@ -384,6 +388,12 @@ extern "C" mad_status mad_mask_slices(int32_t pattern, int32_t T, const mad_mask
           for (int32_t b0 = s0; b0 < e; b0 += P.block) {
             const int32_t b1 = std::min(e, b0 + P.block);
             S.add(b0, b1, s0, b1, F);
+          }
+        } else if (pattern == MAD_MASK_BLOCK_CAUSAL_DOCUMENT_GLOBAL) {
+          // the document's rows in global block [g0, g0 + B) see its keys up to that block's end
+          for (int64_t g0 = (int64_t)s0 / P.block * P.block; g0 < e; g0 += P.block) {
+            const int32_t r0 = (int32_t)std::max<int64_t>(s0, g0), r1 = (int32_t)std::min<int64_t>(e, g0 + P.block);
+            S.add(r0, r1, s0, r1, F);
           }
         } else {
           const int32_t pd = L / 4;
@@ -425,10 +435,58 @@ extern "C" mad_status mad_mask_slices(int32_t pattern, int32_t T, const mad_mask
       }
       break;
     }
+    case MAD_MASK_CAUSAL_BLOCKWISE_LAST: {
+      int32_t last = 0;  // start of the last block
+      for (int64_t b0 = 0; b0 < T; b0 += P.block) {
+        const int32_t b1 = (int32_t)std::min<int64_t>(T, b0 + P.block);
+        S.add((int32_t)b0, b1, (int32_t)b0, b1, C);
+        last = (int32_t)b0;
+      }
+      S.add(last, T, 0, last, F);
+      break;
+    }
     default: return fail(MAD_ERR_INVALID, "mad_mask_slices: unknown pattern " + std::to_string(pattern));
   }
   *n_out = S.n;
   if (out && S.n > cap) return fail(MAD_ERR_INVALID, "mad_mask_slices: cap too small");
+  return MAD_OK;
+}
+
+extern "C" mad_status mad_varlen_slices(const int32_t* cu_q, const int32_t* cu_k, int32_t batch, int32_t causal,
+                                        int32_t window, int32_t bottom_right, mad_slice* out, int64_t cap,
+                                        int64_t* n_out) {
+  clear_error();
+  if (!n_out) return fail(MAD_ERR_INVALID, "mad_varlen_slices: n_out is NULL");
+  if (batch < 0 || (batch > 0 && (!cu_q || !cu_k))) return fail(MAD_ERR_INVALID, "mad_varlen_slices: bad batch / offsets");
+  if (out && cap < 0) return fail(MAD_ERR_INVALID, "mad_varlen_slices: cap < 0");
+  if (window < 0 || (window > 0 && !causal)) return fail(MAD_ERR_INVALID, "mad_varlen_slices: window needs causal");
+  if (batch > 0 && (cu_q[0] != 0 || cu_k[0] != 0)) return fail(MAD_ERR_INVALID, "mad_varlen_slices: offsets must start at 0");
+  for (int32_t b = 0; b < batch; ++b) {
+    if (cu_q[b + 1] < cu_q[b] || cu_k[b + 1] < cu_k[b])
+      return fail(MAD_ERR_INVALID, "mad_varlen_slices: offsets must be non-decreasing");
+    if (causal && bottom_right && window > 0 && cu_k[b + 1] - cu_k[b] > cu_q[b + 1] - cu_q[b])
+      return fail(MAD_ERR_UNSUPPORTED, "mad_varlen_slices: a window with bottom-right alignment needs Lk <= Lq");
+  }
+  SliceSink S{out, cap};
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t q0 = cu_q[b], q1 = cu_q[b + 1], k0 = cu_k[b], k1 = cu_k[b + 1];
+    if (q0 == q1 || k0 == k1) continue;
+    if (!causal) {
+      S.add(q0, q1, k0, k1, MAD_SLICE_FULL);
+    } else if (!bottom_right) {
+      S.add(q0, q1, k0, k1, MAD_SLICE_CAUSAL, window);
+    } else {
+      const int32_t off = (k1 - k0) - (q1 - q0);  // key c is allowed from row c - off on
+      if (off >= 0) {
+        if (off > 0) S.add(q0, q1, k0, k0 + off, MAD_SLICE_FULL);  // keys every row sees
+        S.add(q0, q1, k0 + off, k1, MAD_SLICE_CAUSAL, window);  // window > 0 only when off == 0
+      } else {
+        S.add(q0 - off, q1, k0, k1, MAD_SLICE_CAUSAL, window);  // the first -off rows see nothing
+      }
+    }
+  }
+  *n_out = S.n;
+  if (out && S.n > cap) return fail(MAD_ERR_INVALID, "mad_varlen_slices: cap too small");
   return MAD_OK;
 }
 

@@ -26,6 +26,15 @@ Readings where the pages are silent (each also listed in the design notes):
   * Block Causal Document blocks counted from each document's start
   * sixth heterogeneous mask = PREFIX_LM_DOCUMENT (prefix LM per document,
     p_d = floor(L_d/4)); parity unpinned as to identity
+  * two alternative readings, kept beside the ones the workloads use:
+    CAUSAL_BLOCKWISE_LAST (causal inside each block; only the last block
+    also sees every earlier block, the in-context-learning layout of the
+    FlashMask paper's blockwise mask) and BLOCK_CAUSAL_DOCUMENT_GLOBAL
+    (block edges at multiples of B from token 0 instead of each document's
+    start); parity unpinned as to which one the pages mean
+  * VARLEN: a batch of packed sequences given by cumulative offsets; causal
+    masks aligned top-left (key c <= row r in sequence-local offsets) or
+    bottom-right (c <= r + Lk - Lq)
   * sparsity s (percent) = share of key blocks dropped per query block:
     keep k = n_kb - floor(s*n_kb/100), at least 1; ties in score broken
     toward the lower block index; one keep set per KV head (GQA shares it
@@ -42,11 +51,12 @@ STATIC_PATTERNS = (
     "FULL", "CAUSAL", "SLIDING_WINDOW", "FULL_DOCUMENT", "CAUSAL_DOCUMENT",
     "SLIDING_WINDOW_CAUSAL_DOCUMENT", "PREFIX_LM", "SHARED_QUESTION",
     "GLOBAL_SLIDING", "CAUSAL_BLOCKWISE", "BLOCK_CAUSAL_DOCUMENT",
-    "PREFIX_LM_DOCUMENT",
+    "PREFIX_LM_DOCUMENT", "CAUSAL_BLOCKWISE_LAST", "BLOCK_CAUSAL_DOCUMENT_GLOBAL",
 )
 SPARSE_PATTERNS = ("BLOCK_SPARSE", "VARIABLE_BLOCK_SPARSE")
 RING_PATTERNS = ("RING_STEP",)
 SLICE_PATTERNS = ("SLICES",)
+VARLEN_PATTERNS = ("VARLEN",)
 
 
 @dataclass
@@ -73,6 +83,12 @@ class MaskSpec:
     source: int = 0
     # SLICES: tuples (q0, q1, k0, k1, type 0=full 1=causal, window)
     slices: tuple = ()
+    # VARLEN: cumulative offsets of the packed sequences (length batch + 1)
+    cu_q: tuple = ()
+    cu_k: tuple = ()
+    causal: bool = True
+    bottom_right: bool = False
+    varlen_window: int = 0        # VARLEN causal window (0: none)
 
     @property
     def n_groups(self) -> int:
@@ -151,7 +167,7 @@ def allowed(spec: MaskSpec, rows, cols, group: int = 0) -> np.ndarray:
         W = spec.window
         return (j <= i) & (j > i - W)
     if p in ("FULL_DOCUMENT", "CAUSAL_DOCUMENT", "SLIDING_WINDOW_CAUSAL_DOCUMENT",
-             "BLOCK_CAUSAL_DOCUMENT", "PREFIX_LM_DOCUMENT"):
+             "BLOCK_CAUSAL_DOCUMENT", "PREFIX_LM_DOCUMENT", "BLOCK_CAUSAL_DOCUMENT_GLOBAL"):
         di, si, Li = _doc_index(spec.doc_lens, i)
         dj, _, _ = _doc_index(spec.doc_lens, j)
         same = di == dj
@@ -165,6 +181,9 @@ def allowed(spec: MaskSpec, rows, cols, group: int = 0) -> np.ndarray:
         if p == "BLOCK_CAUSAL_DOCUMENT":
             B = spec.block
             return same & (((j - si) // B) <= ((i - si) // B))
+        if p == "BLOCK_CAUSAL_DOCUMENT_GLOBAL":
+            B = spec.block
+            return same & ((j // B) <= (i // B))
         # PREFIX_LM_DOCUMENT
         pd = Li // 4
         return same & ((j - si) <= np.maximum(i - si, pd - 1))
@@ -183,6 +202,30 @@ def allowed(spec: MaskSpec, rows, cols, group: int = 0) -> np.ndarray:
         B = spec.block
         bi, bj = i // B, j // B
         return (bj < bi) | ((bj == bi) & (j <= i))
+    if p == "CAUSAL_BLOCKWISE_LAST":
+        B = spec.block
+        bi, bj = i // B, j // B
+        last = (T - 1) // B
+        return ((bj == bi) & (j <= i)) | ((bi == last) & (bj < bi))
+    if p == "VARLEN":
+        cq = np.asarray(spec.cu_q, dtype=np.int64)
+        ck = np.asarray(spec.cu_k if spec.cu_k else spec.cu_q, dtype=np.int64)
+        # sequence of each token; tokens past the last offset belong to none
+        bi = np.searchsorted(cq, i, side="right") - 1
+        bj = np.searchsorted(ck, j, side="right") - 1
+        nb = len(cq) - 1
+        ok = (bi >= 0) & (bi < nb) & (bj >= 0) & (bj < nb) & (bi == bj)
+        bic = np.clip(bi, 0, max(nb - 1, 0))
+        bjc = np.clip(bj, 0, max(nb - 1, 0))
+        if not spec.causal or nb == 0:
+            return ok
+        r = i - cq[bic]
+        c = j - ck[bjc]
+        shift = (ck[bic + 1] - ck[bic]) - (cq[bic + 1] - cq[bic]) if spec.bottom_right else 0
+        m = ok & (c <= r + shift)
+        if spec.varlen_window > 0:
+            m &= (r + shift - c) < spec.varlen_window
+        return m
     if p in ("BLOCK_SPARSE", "VARIABLE_BLOCK_SPARSE"):
         qb = np.searchsorted(spec.q_edges, i, side="right") - 1
         kb = np.searchsorted(spec.k_edges, j, side="right") - 1

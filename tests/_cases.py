@@ -22,6 +22,8 @@ def small_specs(T, seed=0):
         MaskSpec("CAUSAL_BLOCKWISE", T, T, block=max(1, T // 3)),
         MaskSpec("BLOCK_CAUSAL_DOCUMENT", T, T, block=max(1, T // 7), doc_lens=docs),
         MaskSpec("PREFIX_LM_DOCUMENT", T, T, doc_lens=docs),
+        MaskSpec("CAUSAL_BLOCKWISE_LAST", T, T, block=max(1, T // 3)),
+        MaskSpec("BLOCK_CAUSAL_DOCUMENT_GLOBAL", T, T, block=max(1, T // 7), doc_lens=docs),
     ]
     return out
 

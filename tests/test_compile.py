@@ -36,7 +36,7 @@ def _assert_plan_matches(plan, spec, group=0, which=(0, 1)):
 
 
 @pytest.mark.parametrize("T", [1, 63, 129, 1000, 2049])
-@pytest.mark.parametrize("idx", range(12))
+@pytest.mark.parametrize("idx", range(len(M.STATIC_PATTERNS)))
 def test_static_patterns_bit_exact(T, idx):
     spec = small_specs(T, seed=idx + T)[idx]
     plan = mad.mask_compile(mad.mask_slices(spec.pattern, T, **spec_kwargs(spec)), T, T)
@@ -71,6 +71,32 @@ def test_random_slices_bit_exact(seed):
     arr = np.array(sl, dtype=mad.SLICE_DTYPE) if sl else np.zeros(0, dtype=mad.SLICE_DTYPE)
     plan = mad.mask_compile(arr, Tq, Tk)
     _assert_plan_matches(plan, M.MaskSpec("SLICES", Tq, Tk, slices=tuple(sl)))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_varlen_slices_bit_exact(seed):
+    """Batches of packed sequences (self and cross attention, empty sequences included),
+    full or causal, top-left or bottom-right, with and without a window."""
+    rng = np.random.default_rng(100 + seed)
+    batch = int(rng.integers(1, 7))
+    lq = rng.integers(0, 300, size=batch)
+    lk = lq.copy() if seed % 2 == 0 else rng.integers(0, 300, size=batch)
+    cq = np.concatenate([[0], np.cumsum(lq)]).astype(np.int64)
+    ck = np.concatenate([[0], np.cumsum(lk)]).astype(np.int64)
+    for causal in (False, True):
+        for br in (False, True):
+            for win in (0, 37):
+                if win and not causal:
+                    continue
+                if win and br and np.any(lk > lq):
+                    with pytest.raises(mad.MadError):
+                        mad.varlen_slices(cq, ck, causal=causal, window=win, bottom_right=br)
+                    continue
+                sl = mad.varlen_slices(cq, ck, causal=causal, window=win, bottom_right=br)
+                spec = M.MaskSpec("VARLEN", int(cq[-1]), int(ck[-1]), cu_q=tuple(cq), cu_k=tuple(ck),
+                                  causal=causal, bottom_right=br, varlen_window=win)
+                plan = mad.mask_compile(sl, spec.Tq, spec.Tk)
+                _assert_plan_matches(plan, spec)
 
 
 @pytest.mark.parametrize("layout", ["contiguous", "headtail"])

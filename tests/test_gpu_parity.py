@@ -50,11 +50,27 @@ def test_tiny_reference_config(pattern):
 
 
 @pytest.mark.parametrize("d", [128, 64])
-@pytest.mark.parametrize("idx", range(12))
+@pytest.mark.parametrize("idx", range(len(M.STATIC_PATTERNS)))
 def test_static_patterns_small(idx, d):
     T = 1000 + 37 * idx  # ragged: never a multiple of the 128 / 64 tile sizes
     spec = small_specs(T, seed=idx)[idx]
     _run_case(spec, _plan_for(spec), 8, 2, d, seed=100 + idx)
+
+
+@pytest.mark.parametrize("bottom_right", [False, True])
+@pytest.mark.parametrize("d", [128, 64])
+def test_varlen_cross_attention(bottom_right, d):
+    """A batch of packed sequences with different query and key lengths (causal; bottom-right
+    alignment leaves the first Lq - Lk rows of a sequence with no key: O = 0, LSE = -inf)."""
+    import mask_aware_dense_amd as mad
+    rng = np.random.default_rng(41 + d)
+    lq, lk = rng.integers(1, 400, size=5), rng.integers(1, 400, size=5)
+    cq = np.concatenate([[0], np.cumsum(lq)]).astype(np.int64)
+    ck = np.concatenate([[0], np.cumsum(lk)]).astype(np.int64)
+    spec = M.MaskSpec("VARLEN", int(cq[-1]), int(ck[-1]), cu_q=tuple(int(x) for x in cq),
+                      cu_k=tuple(int(x) for x in ck), causal=True, bottom_right=bottom_right)
+    plan = mad.mask_compile(mad.varlen_slices(cq, ck, causal=True, bottom_right=bottom_right), spec.Tq, spec.Tk)
+    _run_case(spec, plan, 8, 2, d, seed=300 + d + int(bottom_right))
 
 
 def _sparse(T, b, G, pct, seed, variable):

@@ -262,3 +262,98 @@ def test_slice_union_matches_closed_forms():
     ref = np.tri(T, T, dtype=bool)
     ref[5:9, 0:40] = True
     assert np.array_equal(a, ref)
+
+
+# ---- alternative readings and the varlen layout: special cases and closed forms ----
+
+def _blocks(T, B):
+    return [min(B, T - b0) for b0 in range(0, T, B)]
+
+
+@pytest.mark.parametrize("T,B", [(1000, 333), (1000, 1), (1000, 1000), (1000, 4000), (77, 10), (64, 32)])
+def test_causal_blockwise_last(T, B):
+    """Causal inside each block; the last block also sees all earlier blocks.
+
+    Pair count: every block its own triangle, plus the last block's rows times
+    all earlier keys.  B >= T is CAUSAL; two blocks are CAUSAL too (the last
+    block then sees everything before it); B = 1 is the diagonal plus a full
+    last row (2T - 1 pairs)."""
+    spec = M.MaskSpec("CAUSAL_BLOCKWISE_LAST", T, T, block=B)
+    L = _blocks(T, B)
+    want = sum(x * (x + 1) // 2 for x in L) + L[-1] * (T - L[-1])
+    assert M.pair_count(spec) == want
+    rows = np.arange(T)
+    m = M.allowed(spec, rows, rows)
+    if len(L) <= 2:
+        assert np.array_equal(m, M.allowed(M.MaskSpec("CAUSAL", T, T), rows, rows))
+    if B == 1:
+        assert want == 2 * T - 1
+    # rows outside the last block never look outside their own block
+    bi = rows // B
+    assert not np.any(m & (bi[:, None] != bi[None, :]) & (bi[:, None] != bi[-1]))
+
+
+def test_block_causal_document_global():
+    """Block edges at multiples of B from token 0.
+
+    B >= T gives FULL_DOCUMENT, B = 1 gives CAUSAL_DOCUMENT, and documents
+    that start on multiples of B give the per-document reading."""
+    T = 1000
+    docs = tuple(int(x) for x in doc_lengths(11, T, lo=20, hi=400))
+    rows = np.arange(T)
+
+    def m(p, **kw):
+        return M.allowed(M.MaskSpec(p, T, T, doc_lens=docs, **kw), rows, rows)
+
+    assert np.array_equal(m("BLOCK_CAUSAL_DOCUMENT_GLOBAL", block=T), m("FULL_DOCUMENT"))
+    assert np.array_equal(m("BLOCK_CAUSAL_DOCUMENT_GLOBAL", block=1), m("CAUSAL_DOCUMENT"))
+    aligned = (200, 100, 300, 400)
+    mg = M.allowed(M.MaskSpec("BLOCK_CAUSAL_DOCUMENT_GLOBAL", T, T, doc_lens=aligned, block=100), rows, rows)
+    md = M.allowed(M.MaskSpec("BLOCK_CAUSAL_DOCUMENT", T, T, doc_lens=aligned, block=100), rows, rows)
+    assert np.array_equal(mg, md)
+    # a document [s, e) contributes, per global block g it meets, (rows in the block) x (keys s .. block end)
+    B = 64
+    want, s0 = 0, 0
+    for L in docs:
+        e = s0 + L
+        for g0 in range(s0 // B * B, e, B):
+            r0, r1 = max(s0, g0), min(e, g0 + B)
+            want += (r1 - r0) * (r1 - s0)
+        s0 = e
+    assert M.pair_count(M.MaskSpec("BLOCK_CAUSAL_DOCUMENT_GLOBAL", T, T, doc_lens=docs, block=B)) == want
+
+
+def test_varlen_reduces_to_document_patterns():
+    """With cu_k = cu_q, VARLEN is the document family: FULL_DOCUMENT, CAUSAL_DOCUMENT
+    (either alignment) and SLIDING_WINDOW_CAUSAL_DOCUMENT; one sequence is FULL / CAUSAL."""
+    docs = tuple(int(x) for x in doc_lengths(12, 900, lo=10, hi=300))
+    T = sum(docs)
+    cu = tuple(int(x) for x in np.concatenate([[0], np.cumsum(docs)]))
+    rows = np.arange(T)
+
+    def v(**kw):
+        return M.allowed(M.MaskSpec("VARLEN", T, T, cu_q=cu, **kw), rows, rows)
+
+    def d(p, **kw):
+        return M.allowed(M.MaskSpec(p, T, T, doc_lens=docs, **kw), rows, rows)
+
+    assert np.array_equal(v(causal=False), d("FULL_DOCUMENT"))
+    assert np.array_equal(v(causal=True), d("CAUSAL_DOCUMENT"))
+    assert np.array_equal(v(causal=True, bottom_right=True), d("CAUSAL_DOCUMENT"))
+    assert np.array_equal(v(causal=True, varlen_window=50), d("SLIDING_WINDOW_CAUSAL_DOCUMENT", window=50))
+    one = M.MaskSpec("VARLEN", T, T, cu_q=(0, T), causal=True)
+    assert np.array_equal(M.allowed(one, rows, rows), M.allowed(M.MaskSpec("CAUSAL", T, T), rows, rows))
+
+
+@pytest.mark.parametrize("lq,lk", [(100, 250), (250, 100), (7, 7), (0, 5), (5, 0)])
+def test_varlen_cross_attention_counts(lq, lk):
+    """Cross attention (Lq != Lk) in one sequence of a batch: top-left row r sees keys 0..r,
+    bottom-right row r sees keys 0..r + Lk - Lq (both clipped to [0, Lk))."""
+    pre_q, pre_k = 30, 40  # a first sequence before it
+    cq, ck = (0, pre_q, pre_q + lq), (0, pre_k, pre_k + lk)
+    for br in (False, True):
+        spec = M.MaskSpec("VARLEN", cq[-1], ck[-1], cu_q=cq, cu_k=ck, causal=True, bottom_right=br)
+        sh = lk - lq if br else 0
+        seq2 = sum(min(lk, max(0, r + 1 + sh)) for r in range(lq))
+        seq1 = sum(min(pre_k, max(0, r + 1 + ((pre_k - pre_q) if br else 0))) for r in range(pre_q))
+        assert M.pair_count(spec) == seq1 + seq2
