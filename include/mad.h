@@ -182,6 +182,36 @@ mad_status mad_sparse_plan(int32_t n_groups, const int32_t* q_edges, int32_t n_q
                            const int32_t* k_edges, int32_t n_kb, const uint64_t* keep,
                            mad_plan** out);
 
+/* The same compilation on the GPU, for a keep bitmap already in device
+ * memory (mad_block_mask's output: a dynamic mask of LongCA-bench appendix
+ * A.2 / A.3 that changes every step), so the bitmap never travels to the
+ * host.  The plan is identical to mad_sparse_plan's over the same edges and
+ * bits (visit lists, aux words, longest-first orders, pair and tile counts)
+ * and is already uploaded to the current device (mad_plan_upload is a
+ * no-op for it).
+ *   q_edges / k_edges: host int32, as for mad_sparse_plan.
+ *   keep: device uint64 [n_groups][n_qb][ceil(n_kb / 64)], 8-byte aligned;
+ *     read by kernels queued on `stream` (bits past n_kb are ignored).
+ * Runs its kernels on `stream` and synchronises it once (the plan's device
+ * block is sized from the list lengths), then queues the list fill: the
+ * caller uses the plan on the same stream, or synchronises first.  The
+ * plan owns its device memory (two allocations) until mad_plan_destroy.
+ * mad_plan_export works on it (it copies the group's lists back).
+ * Invalid arguments return an error before anything is launched. */
+mad_status mad_sparse_plan_device(int32_t n_groups, const int32_t* q_edges, int32_t n_qb,
+                                  const int32_t* k_edges, int32_t n_kb, const uint64_t* keep,
+                                  hipStream_t stream, mad_plan** out);
+
+/* The raw visit lists of tiling `which` as the kernels read them (for
+ * inspection and tests): ptr [n_ptr = n_groups * (n_major + 1)] absolute
+ * offsets, ent / ent_aux [n_ent] (entry = minor tile | 1 << 31 for PARTIAL;
+ * aux = slice-list offset (slice masks) or FULL-strip bits / -1 (block
+ * masks)), order [n_order = n_major] longest first.  Any output may be NULL;
+ * n_* receive the sizes.  Host buffers; a GPU-compiled plan is copied back
+ * from the device (synchronously). */
+mad_status mad_plan_lists(const mad_plan* plan, int32_t which, int64_t* n_ptr, int64_t* n_ent,
+                          int64_t* n_order, int32_t* ptr, int32_t* ent, int32_t* ent_aux, int32_t* order);
+
 /* Copy the plan's metadata to the current device (allocates device memory
  * owned by the plan; synchronises `stream`).  Idempotent. */
 mad_status mad_plan_upload(mad_plan* plan, hipStream_t stream);

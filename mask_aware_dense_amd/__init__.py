@@ -15,7 +15,7 @@ import os
 import numpy as np
 
 __all__ = [
-    "MadError", "lib", "Plan", "mask_slices", "ring_step_slices", "varlen_slices", "block_topk",
+    "MadError", "lib", "Plan", "mask_slices", "ring_step_slices", "varlen_slices", "block_topk", "sparse_plan_device",
     "mask_compile", "sparse_plan", "attn_fwd", "attn_bwd", "attn_bwd_phases", "bwd_workspace_bytes",
     "block_mask", "block_mask_workspace_bytes", "lse_merge", "Ring", "BWD_DELTA", "BWD_DKDV", "BWD_DQ", "BWD_ALL",
     "PATTERNS", "SLICE_DTYPE",
@@ -65,6 +65,8 @@ _SIGS = {
     "mad_block_topk": (_I32, [_VP, _I32, _I32, _I32, _I32, _VP]),
     "mad_mask_compile": (_I32, [_VP, _I64, _I32, _I32, ctypes.POINTER(_VP)]),
     "mad_sparse_plan": (_I32, [_I32, _VP, _I32, _VP, _I32, _VP, ctypes.POINTER(_VP)]),
+    "mad_sparse_plan_device": (_I32, [_I32, _VP, _I32, _VP, _I32, _VP, _VP, ctypes.POINTER(_VP)]),
+    "mad_plan_lists": (_I32, [_VP, _I32, _PI64, _PI64, _PI64, _VP, _VP, _VP, _VP]),
     "mad_plan_upload": (_I32, [_VP, _VP]),
     "mad_plan_stats": (_I32, [_VP, _I32, _VP, _PI64, _PI64, _PI64]),
     "mad_plan_info": (_I32, [_VP, _I32, _PI32, _PI32, _PI32, _PI32, _PI32, _PI32, _PI32]),
@@ -234,6 +236,16 @@ class Plan:
         return {"classes": cls.reshape(nq, nk), "csr_ptr": csr_ptr, "csr_idx": csr_idx[:csr_ptr[-1]],
                 "csc_ptr": csc_ptr, "csc_idx": csc_idx[:csc_ptr[-1]]}
 
+    def lists(self, which: int = 0) -> dict:
+        """Raw visit lists of tiling `which` as the kernels read them (ptr, ent, ent_aux, order)."""
+        n = [ctypes.c_int64(0) for _ in range(3)]
+        _check(lib().mad_plan_lists(self.handle, which, *(ctypes.byref(x) for x in n), None, None, None, None))
+        ptr, ent, aux, order = (np.zeros(max(int(x.value), 1), dtype=np.int32) for x in (n[0], n[1], n[1], n[2]))
+        _check(lib().mad_plan_lists(self.handle, which, None, None, None, ptr.ctypes.data, ent.ctypes.data,
+                                    aux.ctypes.data, order.ctypes.data))
+        return {"ptr": ptr[:n[0].value], "ent": ent[:n[1].value], "ent_aux": aux[:n[1].value],
+                "order": order[:n[2].value]}
+
 
 def mask_compile(slices: np.ndarray, Tq: int, Tk: int) -> Plan:
     s = np.ascontiguousarray(slices, dtype=SLICE_DTYPE)
@@ -249,6 +261,17 @@ def sparse_plan(n_groups: int, q_edges, k_edges, keep: np.ndarray) -> Plan:
     h = ctypes.c_void_p()
     _check(lib().mad_sparse_plan(n_groups, qe.ctypes.data, qe.size - 1, ke.ctypes.data, ke.size - 1,
                                  kp.ctypes.data, ctypes.byref(h)))
+    return Plan(h.value)
+
+
+def sparse_plan_device(n_groups: int, q_edges, k_edges, keep, stream=None) -> Plan:
+    """Block-sparse plan compiled on the GPU from a device keep bitmap (torch uint64 tensor
+    [G, n_qb, ceil(n_kb/64)], e.g. block_mask's output); edges are host arrays."""
+    qe = np.ascontiguousarray(q_edges, dtype=np.int32)
+    ke = np.ascontiguousarray(k_edges, dtype=np.int32)
+    h = ctypes.c_void_p()
+    _check(lib().mad_sparse_plan_device(n_groups, qe.ctypes.data, qe.size - 1, ke.ctypes.data, ke.size - 1,
+                                        _ptr(keep), _stream(stream), ctypes.byref(h)))
     return Plan(h.value)
 
 

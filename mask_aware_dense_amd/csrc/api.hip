@@ -227,6 +227,7 @@ extern "C" void mad_plan_destroy(mad_plan* p) {
     (void)hipGetDevice(&cur);
     if (cur != p->dev_id) (void)hipSetDevice(p->dev_id);
     (void)hipFree(p->dev_mem);
+    if (p->dev_tmp) (void)hipFree(p->dev_tmp);
     if (cur != p->dev_id && cur >= 0) (void)hipSetDevice(cur);
   }
   delete p;

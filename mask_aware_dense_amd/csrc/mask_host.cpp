@@ -664,6 +664,33 @@ extern "C" mad_status mad_plan_stats(const mad_plan* p, int32_t which, int64_t* 
   return MAD_OK;
 }
 
+extern "C" mad_status mad_plan_lists(const mad_plan* p, int32_t which, int64_t* n_ptr, int64_t* n_ent,
+                                     int64_t* n_order, int32_t* ptr, int32_t* ent, int32_t* ent_aux, int32_t* order) {
+  clear_error();
+  if (!p) return fail(MAD_ERR_INVALID, "mad_plan_lists: plan is NULL");
+  if (which != 0 && which != 1) return fail(MAD_ERR_INVALID, "mad_plan_lists: which must be 0 or 1");
+  const TilingHost& t = p->tiling[which];
+  const int64_t np = (int64_t)t.ptr.size(), ne = t.ptr.empty() ? 0 : t.ptr.back();
+  const int64_t no = which == 0 ? t.nqt : t.nkt;
+  if (n_ptr) *n_ptr = np;
+  if (n_ent) *n_ent = ne;
+  if (n_order) *n_order = no;
+  if (ptr && np) std::memcpy(ptr, t.ptr.data(), (size_t)np * 4);
+  if (!p->on_device) {
+    if (ent && ne) std::memcpy(ent, t.ent.data(), (size_t)ne * 4);
+    if (ent_aux && ne) std::memcpy(ent_aux, t.ent_aux.data(), (size_t)ne * 4);
+    if (order && no) std::memcpy(order, t.order.data(), (size_t)no * 4);
+    return MAD_OK;
+  }
+  const TilingDev& d = p->tdev[which];
+  hipError_t e = hipSuccess;
+  if (ent && ne && e == hipSuccess) e = hipMemcpy(ent, d.ent, (size_t)ne * 4, hipMemcpyDeviceToHost);
+  if (ent_aux && ne && e == hipSuccess) e = hipMemcpy(ent_aux, d.ent_aux, (size_t)ne * 4, hipMemcpyDeviceToHost);
+  if (order && no && e == hipSuccess) e = hipMemcpy(order, d.order, (size_t)no * 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(MAD_ERR_HIP, std::string("mad_plan_lists: hipMemcpy: ") + hipGetErrorString(e));
+  return MAD_OK;
+}
+
 extern "C" mad_status mad_plan_info(const mad_plan* p, int32_t which, int32_t* Tq, int32_t* Tk, int32_t* n_groups,
                                     int32_t* BM, int32_t* BN, int32_t* n_qt, int32_t* n_kt) {
   clear_error();
@@ -687,7 +714,27 @@ extern "C" mad_status mad_plan_export(const mad_plan* p, int32_t which, int32_t 
   if (which != 0 && which != 1) return fail(MAD_ERR_INVALID, "mad_plan_export: which must be 0 or 1");
   if (group < 0 || group >= p->G) return fail(MAD_ERR_INVALID, "mad_plan_export: group out of range");
   const TilingHost& t = p->tiling[which];
-  const auto& cls = t.cls[group];
+  std::vector<uint8_t> dev_cls;
+  if (p->on_device) {
+    // classes rebuilt from the group's visit lists, copied back from the device
+    const int nmaj = which == 0 ? t.nqt : t.nkt;
+    const int32_t* gp = t.ptr.data() + (size_t)group * (nmaj + 1);
+    const int64_t n = gp[nmaj] - gp[0];
+    std::vector<int32_t> ent(n);
+    if (n > 0) {
+      hipError_t e = hipMemcpy(ent.data(), p->tdev[which].ent + gp[0], (size_t)n * 4, hipMemcpyDeviceToHost);
+      if (e != hipSuccess) return fail(MAD_ERR_HIP, std::string("mad_plan_export: hipMemcpy: ") + hipGetErrorString(e));
+    }
+    dev_cls.assign((size_t)t.nqt * t.nkt, CLS_EMPTY);
+    for (int M = 0; M < nmaj; ++M)
+      for (int32_t x = gp[M]; x < gp[M + 1]; ++x) {
+        const uint32_t en = (uint32_t)ent[x - gp[0]];
+        const int m = (int)(en & 0x7fffffffu);
+        const int64_t tile = which == 0 ? (int64_t)M * t.nkt + m : (int64_t)m * t.nkt + M;
+        dev_cls[tile] = (en & ENT_PARTIAL) ? CLS_PARTIAL : CLS_FULL;
+      }
+  }
+  const auto& cls = p->on_device ? dev_cls : t.cls[group];
   if (classes) std::memcpy(classes, cls.data(), cls.size());
   if (csr_ptr || csr_idx) {
     int64_t n = 0;

@@ -96,6 +96,11 @@ struct mad_plan {
   void* dev_mem = nullptr;
   int dev_id = -1;
   size_t dev_bytes = 0;
+  // plans compiled on the GPU (mad_sparse_plan_device): the builder's scratch,
+  // freed with the plan, and no host copy of the tile classes or list entries
+  // (host ptr arrays, class counts and pairs are kept)
+  void* dev_tmp = nullptr;
+  bool on_device = false;
   mad::TilingDev tdev[2] = {};
   mad::MaskDev mdev = {};
 };

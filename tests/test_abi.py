@@ -177,3 +177,41 @@ def test_block_mask_errors():
     assert call(ws=16) == 1           # workspace too small
     assert L.mad_block_mask(None, p, 1024, 1024, 8, 2, 128, 2, p, 8, p, 8, 50, ctypes.c_float(0.1), p, 1 << 20,
                             p, None, None) == 1
+
+
+def test_sparse_plan_device_errors():
+    """Argument checks of the GPU plan compiler fail before any device work."""
+    L = mad.lib()
+    qe = np.array([0, 64, 128], dtype=np.int32)
+    ke = np.array([0, 64, 100], dtype=np.int32)
+    bad = np.array([0, 64, 64], dtype=np.int32)
+    keep = ctypes.c_void_p(4096)
+    out = ctypes.c_void_p()
+
+    def call(G=2, q=qe, nqb=2, k=ke, nkb=2, kp=keep, o=ctypes.byref(out)):
+        return L.mad_sparse_plan_device(G, q.ctypes.data if q is not None else None, nqb,
+                                        k.ctypes.data if k is not None else None, nkb, kp, None, o)
+
+    assert call(o=None) == 1
+    assert call(kp=None) == 1
+    assert call(q=None) == 1
+    assert call(G=0) == 1
+    assert call(nkb=0) == 1
+    assert call(k=bad) == 1                      # not strictly increasing
+    assert call(q=np.array([1, 64, 128], dtype=np.int32)) == 1  # does not start at 0
+    assert call(kp=ctypes.c_void_p(4100)) == 1   # keep not 8-byte aligned
+    assert out.value is None
+
+
+def test_plan_lists_host_plan():
+    """Raw lists of a host-compiled plan agree with its export (CSR for tiling 0, CSC for tiling 1)."""
+    T = 700
+    plan = mad.mask_compile(mad.mask_slices("CAUSAL", T), T, T)
+    for w in (0, 1):
+        li = plan.lists(w)
+        ex = plan.export(w, 0)
+        ptr = ex["csr_ptr"] if w == 0 else ex["csc_ptr"]
+        idx = ex["csr_idx"] if w == 0 else ex["csc_idx"]
+        assert np.array_equal(li["ptr"], ptr)
+        assert np.array_equal(li["ent"] & 0x7fffffff, idx)
+        assert sorted(li["order"].tolist()) == list(range(len(ptr) - 1))
