@@ -61,7 +61,45 @@ def test_causal_32k_gqa_64_8():
     _check_bwd_invariants(got, do, np.ones((32768, 64), bool), 8)
 
 
-@pytest.mark.parametrize("pattern", ["SLIDING_WINDOW_CAUSAL_DOCUMENT", "SHARED_QUESTION", "BLOCK_CAUSAL_DOCUMENT"])
+def test_global_sliding_32k_gqa_64_8():
+    """GLOBAL_SLIDING at the suite's shape (256 global keys, 2K window): its two global key tiles
+    hold most of the dK/dV items, so their columns are cut between workgroups (fp32 sums)."""
+    T = 32768
+    spec = M.MaskSpec("GLOBAL_SLIDING", T, T, global_len=256, window=2048)
+    q, k, v, do, scale, got = _full_run(spec, 64, 8, 128, seed=6)
+    _check_sampled(spec, q, k, v, do, scale, got, n_rows=24, heads=[0, 13, 63])
+    _check_bwd_invariants(got, do, np.ones((T, 64), bool), 8)
+
+
+def test_block_sparse_32k_gpu_plan():
+    """Block-sparse 32K GQA 64:8, b=128, half the key blocks dropped, with the plan compiled on
+    the GPU from a device keep bitmap: sampled rows against the oracle."""
+    import torch
+    import mask_aware_dense_amd as mad
+    from mad_inputs import block_scores
+    T, b, G = 32768, 128, 8
+    edges = np.asarray(M.uniform_edges(T, b), dtype=np.int32)
+    n = len(edges) - 1
+    keep = M.topk_keep(block_scores(17, G, n, n), 50)
+    plan = mad.sparse_plan(G, edges, edges, mad.block_topk(block_scores(17, G, n, n), 50))
+    words = np.zeros((G, n, (n + 63) // 64), dtype=np.uint64)
+    for j in range(n):
+        words[:, :, j // 64] |= keep[:, :, j].astype(np.uint64) << np.uint64(j % 64)
+    dplan = mad.sparse_plan_device(G, edges, edges, torch.from_numpy(words.view(np.int64)).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(plan.lists(0)["ent"], dplan.lists(0)["ent"])
+    spec = M.MaskSpec("BLOCK_SPARSE", T, T, q_edges=edges, k_edges=edges, keep=keep)
+    q, k, v = qkv(17, T, T, 64, 8, 128)
+    do = grad_out(17, T, 64, 128)
+    scale = 1.0 / np.sqrt(128)
+    print("case BLOCK_SPARSE 32K GQA 64:8 b128 s0.5 (GPU plan)", flush=True)
+    got = _gpu.gpu_attention(dplan, q, k, v, do, scale)
+    _check_sampled(spec, q, k, v, do, scale, got, n_rows=16, seed=5, heads=[0, 9, 63])
+    _check_bwd_invariants(got, do, np.ones((T, 64), bool), 8)
+
+
+@pytest.mark.parametrize("pattern", ["SLIDING_WINDOW_CAUSAL_DOCUMENT", "SHARED_QUESTION", "BLOCK_CAUSAL_DOCUMENT",
+                                     "CAUSAL_BLOCKWISE_LAST", "BLOCK_CAUSAL_DOCUMENT_GLOBAL"])
 def test_16k_workload_masks(pattern):
     T = 16384
     docs = tuple(int(x) for x in doc_lengths(11, T))
