@@ -33,7 +33,9 @@ namespace mad {
 template <int D>
 __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
   constexpr int BM = BM1, BN = BN1, NKS = D / 16, NDB = D / 32;
-  constexpr int TILE = tile_elems<D, TILE_MIXED>(), RS = tile_rs<D, TILE_MIXED>();
+  // D = 128: unpadded swizzled Q / dO tiles; D = 64: padded rows.
+  constexpr int KIND = D == 128 ? TILE_SWZ : TILE_MIXED;
+  constexpr int TILE = tile_elems<D, KIND>(), RS = tile_rs<D, KIND>();
   constexpr int S1 = 2 * NKS;   // phase-1 steps (block, k-step)
   constexpr int S2 = 4 * NDB;   // phase-2 steps (block, t2, d-block)
   constexpr int EB = 16 / NKS;  // P / dS elements per stage-B step
@@ -162,7 +164,13 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
     return cu;
   };
   const uint32_t smem_lds = lds_addr(smem), rowv_lds = lds_addr(&rowv[0][0]);
-  TileLoader<D, TILE_MIXED, 4, false> qload, dload;
+  TileLoader<D, KIND, 4, false> qload, dload;
+  SwzRows srow;
+  SwzTr str;
+  if constexpr (KIND == TILE_SWZ) {
+    srow.init(li, hh);
+    str.init(lane);
+  }
   qload.init(P.q_tok, w, lane);
   dload.init((int64_t)P.Hq * D, w, lane);
   auto issue = [&](const Cursor& cu, int buf) {
@@ -240,18 +248,32 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
       // Phase-1 operands of step st: Q and dO rows b*32 + li, columns 16ks + 8hh.
       bf16x8 opq[3], opd[3];
       auto ld1 = [&](int st) {
-        const int b = st / NKS, ks = st % NKS, off = (b * 32 + li) * RS + 16 * ks + 8 * hh;
-        opq[st % 3] = ld16(Qs + off);
-        opd[st % 3] = ld16(Ds + off);
+        const int b = st / NKS, ks = st % NKS;
+        if constexpr (KIND == TILE_SWZ) {
+          const uint32_t off = srow.o[ks] + b * 32 * 256;
+          opq[st % 3] = ld16((const bf16*)((const char*)Qs + off));
+          opd[st % 3] = ld16((const bf16*)((const char*)Ds + off));
+        } else {
+          const int off = (b * 32 + li) * RS + 16 * ks + 8 * hh;
+          opq[st % 3] = ld16(Qs + off);
+          opd[st % 3] = ld16(Ds + off);
+        }
       };
       // Phase-2 operands of step st: dO and Q read transposed; contraction
       // element e of half-wave hh is query row b*32 + 16 t2 + 8(e/4) + 4hh + e%4.
       bf16x8 trd[3], trq[3];
       auto ld2 = [&](int st) {
         const int b = st / (2 * NDB), t2 = (st / NDB) % 2, db = st % NDB;
-        const int qrow = b * 32 + 16 * t2 + 4 * hh + tr_row(lane), col = db * 32 + tr_col(lane);
-        trd[st % 3] = ld_tr8(Ds + qrow * RS + col, Ds + (qrow + 8) * RS + col);
-        trq[st % 3] = ld_tr8(Qs + qrow * RS + col, Qs + (qrow + 8) * RS + col);
+        if constexpr (KIND == TILE_SWZ) {
+          const uint32_t rb = (b * 32 + 16 * t2) * 256;
+          const char *dc = (const char*)Ds, *qc = (const char*)Qs;
+          trd[st % 3] = ld_tr8((const bf16*)(dc + rb + str.o0[db]), (const bf16*)(dc + rb + str.o1[db]));
+          trq[st % 3] = ld_tr8((const bf16*)(qc + rb + str.o0[db]), (const bf16*)(qc + rb + str.o1[db]));
+        } else {
+          const int qrow = b * 32 + 16 * t2 + 4 * hh + tr_row(lane), col = db * 32 + tr_col(lane);
+          trd[st % 3] = ld_tr8(Ds + qrow * RS + col, Ds + (qrow + 8) * RS + col);
+          trq[st % 3] = ld_tr8(Qs + qrow * RS + col, Qs + (qrow + 8) * RS + col);
+        }
       };
       // P = exp2(c S) and dS = P dP for registers r, r + 1 of block b,
       // written as bf16 straight into the phase-2 A operands: register r

@@ -120,14 +120,50 @@ __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1)
 //           stride is 16 mod 32 dwords (320 B for D=128, 192 B for D=64).
 //   MIXED - both; 304 B (D=128) / 144 B (D=64) keeps row reads conflict-free
 //           and transposed reads at two-way conflicts.
+//   SWZ   - both, D=128 only, unpadded 256-byte rows: storage row p keeps
+//           16-byte chunk c at chunk c ^ swz(p), swz(p) = (p%4)*4 + (p/4)%4.
+//           A row-read pass (16 rows, one chunk) then meets 16 distinct
+//           chunks, and a transposed pass (4 rows x one aligned 64-byte
+//           window) meets 4 distinct windows: both are conflict-free, and the
+//           direct loads carry no pad bytes (they cost LDS time per byte
+//           written).  Addresses are affine only per chunk, so readers keep a
+//           few per-lane offsets (SwzRows, SwzTr).
 // Padding keeps every address affine in the row and column, so operand reads
 // use immediate offsets from one per-lane base.
-enum TileKind { TILE_ROWS = 0, TILE_TR = 1, TILE_MIXED = 2 };
+enum TileKind { TILE_ROWS = 0, TILE_TR = 1, TILE_MIXED = 2, TILE_SWZ = 3 };
 template <int D, int KIND>
 constexpr int tile_rs() {
-  return D == 128 ? (KIND == TILE_ROWS ? 136 : KIND == TILE_TR ? 160 : 152)
+  static_assert(KIND != TILE_SWZ || D == 128, "the swizzled tile is for D = 128");
+  return D == 128 ? (KIND == TILE_ROWS ? 136 : KIND == TILE_TR ? 160 : KIND == TILE_SWZ ? 128 : 152)
                   : (KIND == TILE_TR ? 96 : 72);
 }
+// Chunk permutation of storage row p of a SWZ tile.
+__device__ __forceinline__ int swz_row(int p) { return ((p & 3) << 2) | ((p >> 2) & 3); }
+
+// Byte offsets of one lane's 16-byte row reads in a SWZ tile: storage row
+// li (+ multiples of 16 rows, added by the caller), elements 16 ks + 8 hh.
+struct SwzRows {
+  uint32_t o[8];
+  __device__ __forceinline__ void init(int li, int hh) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) o[ks] = (uint32_t)(li * 256 + 16 * ((2 * ks + hh) ^ swz_row(li)));
+  }
+};
+// Byte offsets of one lane's transposed reads (ld_tr8) in a SWZ tile: rows
+// r = 4 hh + tr_row(lane) and r + 8 (+ multiples of 16 rows), columns
+// 32 db + tr_col(lane).
+struct SwzTr {
+  uint32_t o0[4], o1[4];
+  __device__ __forceinline__ void init(int lane) {
+    const int hh = lane >> 5, r = 4 * hh + tr_row(lane);
+    const int ch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1), half = 8 * (lane & 1);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      o0[db] = (uint32_t)(r * 256 + 16 * ((4 * db + ch) ^ swz_row(r)) + half);
+      o1[db] = (uint32_t)((r + 8) * 256 + 16 * ((4 * db + ch) ^ swz_row(r + 8)) + half);
+    }
+  }
+};
 template <int D, int KIND>
 constexpr int tile_elems() { return 64 * tile_rs<D, KIND>(); }
 
@@ -221,12 +257,17 @@ struct TileLoader {
   static constexpr int SPR = tile_rs<D, KIND>() / 8, CPR = D / 8, NI = (SPR + NW - 1) / NW;
   uint32_t off[NI];  // byte offset of this lane's source chunk from the tile's first row
 
+  // Tensor chunk held by storage slot (row p, chunk c); pad slots repeat chunk 0.
+  static __device__ __forceinline__ int src_chunk(int p, int c) {
+    return c >= CPR ? 0 : (KIND == TILE_SWZ ? c ^ swz_row(p) : c);
+  }
+
   __device__ __forceinline__ void init(int64_t tok, int w, int lane) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int s = (i * NW + w) * 64 + lane;
       const int p = s / SPR, c = s % SPR;
-      off[i] = (uint32_t)(((int64_t)tile_row(p, PERM) * tok + (c < CPR ? c : 0) * 8) * 2);
+      off[i] = (uint32_t)(((int64_t)tile_row(p, PERM) * tok + src_chunk(p, c) * 8) * 2);
     }
   }
   // lds: LDS byte address of the tile image; g: the tensor's head; tok: its
@@ -249,7 +290,7 @@ struct TileLoader {
           const int s = ii * 64 + lane;
           const int p = s / SPR, c = s % SPR;
           const int row = min(r0 + tile_row(p, PERM), T - 1);
-          g2lds16(g + (int64_t)row * tok + (c < CPR ? c : 0) * 8, lds + ii * 1024);
+          g2lds16(g + (int64_t)row * tok + src_chunk(p, c) * 8, lds + ii * 1024);
         }
       }
     }
