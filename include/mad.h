@@ -202,6 +202,13 @@ mad_status mad_sparse_plan_device(int32_t n_groups, const int32_t* q_edges, int3
                                   const int32_t* k_edges, int32_t n_kb, const uint64_t* keep,
                                   hipStream_t stream, mad_plan** out);
 
+/* Measurement aid: n_workgroups workgroups of 4 waves each issue 4 * iters
+ * back-to-back bf16 MFMAs (v_mfma_f32_32x32x16_bf16, 32768 FLOP each) on
+ * register operands, with no memory traffic, so timing the launch gives the
+ * matrix cores' sustained rate at the clock they hold under that load.
+ * sink: device float [n_workgroups], written (one value per workgroup). */
+mad_status mad_probe_mfma(int32_t n_workgroups, int32_t iters, float* sink, hipStream_t stream);
+
 /* The raw visit lists of tiling `which` as the kernels read them (for
  * inspection and tests): ptr [n_ptr = n_groups * (n_major + 1)] absolute
  * offsets, ent / ent_aux [n_ent] (entry = minor tile | 1 << 31 for PARTIAL;

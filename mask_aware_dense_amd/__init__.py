@@ -67,6 +67,7 @@ _SIGS = {
     "mad_sparse_plan": (_I32, [_I32, _VP, _I32, _VP, _I32, _VP, ctypes.POINTER(_VP)]),
     "mad_sparse_plan_device": (_I32, [_I32, _VP, _I32, _VP, _I32, _VP, _VP, ctypes.POINTER(_VP)]),
     "mad_plan_lists": (_I32, [_VP, _I32, _PI64, _PI64, _PI64, _VP, _VP, _VP, _VP]),
+    "mad_probe_mfma": (_I32, [_I32, _I32, _VP, _VP]),
     "mad_plan_upload": (_I32, [_VP, _VP]),
     "mad_plan_stats": (_I32, [_VP, _I32, _VP, _PI64, _PI64, _PI64]),
     "mad_plan_info": (_I32, [_VP, _I32, _PI32, _PI32, _PI32, _PI32, _PI32, _PI32, _PI32]),

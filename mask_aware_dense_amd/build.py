@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmad.so")
 SOURCES = ["api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_dkdv.hip", "ring.hip", "blockmask.hip", "plan_gpu.hip",
-           "mask_host.cpp"]
+           "probe.hip", "mask_host.cpp"]
 ARCH = os.environ.get("MAD_OFFLOAD_ARCH", "gfx950")
 
 

@@ -215,3 +215,10 @@ def test_plan_lists_host_plan():
         assert np.array_equal(li["ptr"], ptr)
         assert np.array_equal(li["ent"] & 0x7fffffff, idx)
         assert sorted(li["order"].tolist()) == list(range(len(ptr) - 1))
+
+
+def test_probe_mfma_errors():
+    L = mad.lib()
+    assert L.mad_probe_mfma(0, 10, ctypes.c_void_p(4096), None) == 1
+    assert L.mad_probe_mfma(4, 0, ctypes.c_void_p(4096), None) == 1
+    assert L.mad_probe_mfma(4, 10, None, None) == 1
