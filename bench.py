@@ -311,10 +311,10 @@ def run_suite(args, torch, mad):
         fwdbwd = 14.0 * d * pairs * args.steps / wall / 1e12
         seeds = None
         if n_seeds > 1 and multi_sequence(name):
-            # the same mask family over further document-length samples: each its own plan,
-            # inputs and timing (a shorter run per sample); the line reports the median
+            # the same mask family over further document-length samples, each with its own plan
+            # and the same warm-up and step counts; the line reports the median
             vals = [fwdbwd]
-            n2 = max(2, args.steps // 2)
+            n2 = args.steps
             for extra in other_seeds:
                 p2, Tq2, Tk2, Hq2, Hkv2, d2, _ = extra[name](mad)
                 p2.upload()
@@ -325,7 +325,7 @@ def run_suite(args, torch, mad):
                     r2.use_plan(p2, Tq2, Tk2, Hq2, Hkv2, d2)
                 else:  # a varlen sample of another total length
                     r2 = Runner(torch, mad, p2, Tq2, Tk2, Hq2, Hkv2, d2, args.seed)
-                w2, _, _ = r2.time(n2, max(1, args.warmup // 2))
+                w2, _, _ = r2.time(n2, args.warmup)
                 vals.append(14.0 * d2 * pr2 * n2 / w2 / 1e12)
                 del r2, p2
             seeds = {"n": len(vals), "median": float(np.median(vals)), "min": float(min(vals)),
