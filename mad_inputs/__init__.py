@@ -17,7 +17,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "qkv", "grad_out", "doc_lengths", "block_scores", "variable_block_sizes",
+    "qkv", "grad_out", "qkv_device", "grad_out_device", "doc_lengths", "block_scores", "variable_block_sizes",
 ]
 
 
@@ -45,6 +45,26 @@ def grad_out(seed: int, Tq: int, Hq: int, d: int):
     torch = _torch()
     g = torch.Generator(device="cpu").manual_seed(int(seed) * 1000003 + 7)
     return torch.randn((Tq, Hq, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+
+
+def qkv_device(seed: int, Tq: int, Tk: int, Hq: int, Hkv: int, d: int, device="cuda"):
+    """The same distribution drawn on the GPU (for the largest sizes, where the CPU generator
+    would take minutes): N(0,1) fp32 from one device generator seeded with `seed`, in the order
+    Q, K, V, rounded to bf16.  Deterministic for a seed on a given device type; the values
+    differ from qkv's, so a test copies back what its oracle needs."""
+    torch = _torch()
+    g = torch.Generator(device=device).manual_seed(int(seed))
+    q = torch.randn((Tq, Hq, d), generator=g, dtype=torch.float32, device=device).to(torch.bfloat16)
+    k = torch.randn((Tk, Hkv, d), generator=g, dtype=torch.float32, device=device).to(torch.bfloat16)
+    v = torch.randn((Tk, Hkv, d), generator=g, dtype=torch.float32, device=device).to(torch.bfloat16)
+    return q, k, v
+
+
+def grad_out_device(seed: int, Tq: int, Hq: int, d: int, device="cuda"):
+    """dO [Tq,Hq,d] bf16 drawn on the GPU from its own stream (seed, tag 7)."""
+    torch = _torch()
+    g = torch.Generator(device=device).manual_seed(int(seed) * 1000003 + 7)
+    return torch.randn((Tq, Hq, d), generator=g, dtype=torch.float32, device=device).to(torch.bfloat16)
 
 
 def doc_lengths(seed: int, T: int, lo: int = 512, hi: int = 16384) -> np.ndarray:
