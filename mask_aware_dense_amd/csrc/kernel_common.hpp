@@ -118,8 +118,11 @@ __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1)
 //   TR    - transposed reads (ds_read_b64_tr_b16): 32 lanes per pass read
 //           64 bytes of each of 4 consecutive rows; conflict-free when the
 //           stride is 16 mod 32 dwords (320 B for D=128, 192 B for D=64).
-//   MIXED - both; 304 B (D=128) / 144 B (D=64) keeps row reads conflict-free
-//           and transposed reads at two-way conflicts.
+//   MIXED - both; 304 B (D=128) / 144 B (D=64) keeps row reads conflict-free.
+//           A pure-read probe shows two-way conflicts on transposed reads at
+//           this stride, but in the kernels' access order (a wave's 32 lanes
+//           reading 4 rows of one 64-byte column block) the counter stays at
+//           zero once the direct-load writes are taken away.
 //   SWZ   - both, D=128 only, unpadded 256-byte rows: storage row p keeps
 //           16-byte chunk c at chunk c ^ swz(p), swz(p) = (p%4)*4 + (p/4)%4.
 //           A row-read pass (16 rows, one chunk) then meets 16 distinct
