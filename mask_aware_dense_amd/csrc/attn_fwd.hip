@@ -27,8 +27,18 @@ namespace mad {
 
 // NB: 32-row query blocks per wave (the workgroup's 128 rows are spread over
 // 4 / NB waves).
+#ifndef FWD_PRE_B
+#define FWD_PRE_B 1
+#endif
+#ifndef FWD_PRE_C
+#define FWD_PRE_C 3
+#endif
 template <int D, int NB>
 __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
+  // Score steps of the next key block issued before a block's max is taken
+  // (stage B) and P V steps issued before the next block's max (stage C).
+  constexpr int PRE_B = FWD_PRE_B < D / 16 - 1 ? FWD_PRE_B : D / 16 - 1;
+  constexpr int PRE_C = FWD_PRE_C < D / 16 - 1 ? FWD_PRE_C : D / 16 - 1;
   constexpr int BM = BM0, BN = BN0, NKS = D / 16, NDB = D / 32, NW = 4 / NB;
   constexpr int KRS = tile_rs<D, TILE_ROWS>(), KT = tile_elems<D, TILE_ROWS>();
   constexpr int VRS = tile_rs<D, TILE_TR>(), VT = tile_elems<D, TILE_TR>();
@@ -208,11 +218,16 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
       __builtin_amdgcn_sched_barrier(0);
     }
     // Stage B: scores of key block 1 under the softmax of block 0.  Its first
-    // step is issued before block 0's max is taken, so the matrix cores stay
-    // busy while the vector unit waits for block 0's last products.
-    ldk(NKS + 2);
-    s_step(NKS);
-    __builtin_amdgcn_sched_barrier(0);
+    // PRE_B steps are issued before block 0's max is taken, so the matrix
+    // cores stay busy while the vector unit waits for block 0's last products
+    // and reduces them.
+#pragma unroll
+    for (int st = NKS; st < NKS + PRE_B; ++st) {
+      if (st + 2 < 2 * NKS) ldk(st + 2);
+      else ldv(st + 2 - 2 * NKS);
+      s_step(st);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     {
       float tmax[2];
       if (block_max(0, tmax)) {
@@ -231,22 +246,26 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
       set_use();
     }
     constexpr int NE = 16 * NB;  // softmax elements per key block and lane
-    constexpr int EB = 2 * ((NE / 2 + NKS - 2) / (NKS - 1));  // block-0 elements per remaining stage-B step (even)
+    constexpr int RB = NKS - PRE_B;                      // remaining stage-B steps
+    constexpr int EB = 2 * ((NE / 2 + RB - 1) / RB);     // block-0 elements per remaining stage-B step (even)
 #pragma unroll
-    for (int st = NKS + 1; st < 2 * NKS; ++st) {
+    for (int st = NKS + PRE_B; st < 2 * NKS; ++st) {
       if (st + 2 < 2 * NKS) ldk(st + 2);
       else ldv(st + 2 - 2 * NKS);
       s_step(st);
 #pragma unroll
-      for (int e = (st - NKS - 1) * EB; e < (st - NKS) * EB && e < NE; e += 2) softmax2(0, e);
+      for (int e = (st - NKS - PRE_B) * EB; e < (st - NKS - PRE_B + 1) * EB && e < NE; e += 2) softmax2(0, e);
       __builtin_amdgcn_sched_barrier(0);
     }
     // Stage C: O^T += V^T P^T for key block 0 under the softmax of block 1.
     // Block 1's reference is settled first; the accumulator's rescale (which
     // must include block 0's products) waits until they are in.
-    ldv(2);
-    pv_step(0);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < PRE_C; ++st) {
+      ldv(st + 2);
+      pv_step(st);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     float alpha1[2] = {1.f, 1.f};
     bool resc1;
     {
@@ -263,13 +282,14 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
       }
       set_use();
     }
-    constexpr int EC = 2 * ((NE / 2 + 2 * NDB - 2) / (2 * NDB - 1));  // block-1 elements per remaining stage-C step
+    constexpr int RC = 2 * NDB - PRE_C;                  // remaining stage-C steps
+    constexpr int EC = 2 * ((NE / 2 + RC - 1) / RC);     // block-1 elements per remaining stage-C step (even)
 #pragma unroll
-    for (int st = 1; st < 2 * NDB; ++st) {
+    for (int st = PRE_C; st < 2 * NDB; ++st) {
       ldv(st + 2);
       pv_step(st);
 #pragma unroll
-      for (int e = (st - 1) * EC; e < st * EC && e < NE; e += 2) softmax2(1, e);
+      for (int e = (st - PRE_C) * EC; e < (st - PRE_C + 1) * EC && e < NE; e += 2) softmax2(1, e);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (resc1) {
