@@ -53,6 +53,14 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, li = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, wave-uniform
   const int row_base = qt * BM + w * 32 * NB;
+  // Block-sparse masks: the keep bitmap rows of this lane's query blocks.
+  const bool blocks = P.m.mode == MODE_BLOCKS;
+  const uint64_t* krow[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    krow[b] = blocks ? P.m.keep + ((size_t)mg * P.m.n_qb + P.m.row_qb[min(row_base + b * 32 + li, P.Tq - 1)]) *
+                                      P.m.nw
+                     : nullptr;
 
   const int32_t* ptr = P.t.ptr + (int64_t)mg * (P.t.nmajor + 1);
   const int beg = sld(ptr + qt), end = sld(ptr + qt + 1);
@@ -107,12 +115,21 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
     const bool masked = (partial && !parts) || ragged;
     uint32_t mbits[2][2];
     if (masked) {
+      if (blocks && partial) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b) {
+          const uint64_t kbits = keymask64_blocks(P.m, krow[b], row_base + b * 32 + li, kt * BN);
+          mbits[b][0] = (uint32_t)kbits;
+          mbits[b][1] = (uint32_t)(kbits >> 32);
+        }
+      } else {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          mbits[b][kb] = keymask32(P.m, aux, mg, partial, row_base + b * 32 + li, kt * BN + kb * 32, row_base,
-                                   row_base + 32 * NB - 1);
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            mbits[b][kb] = keymask32(P.m, aux, mg, partial, row_base + b * 32 + li, kt * BN + kb * 32, row_base,
+                                     row_base + 32 * NB - 1);
+      }
       wait_vmem();
     }
     if (it + 1 < end) issue(sld(P.t.ent + it + 1) & 0x7fffffff, buf ^ 1);

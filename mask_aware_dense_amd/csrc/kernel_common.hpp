@@ -378,6 +378,35 @@ __device__ __forceinline__ uint64_t range_bits64(int a, int b) {
   return hi & ~((1ull << a) - 1ull);
 }
 
+// Block-sparse mask of a kernel whose lanes keep their query row for the
+// whole workgroup (the forward): keys [key0, key0 + 64) that row i may see,
+// the same predicate as keymask32 in MODE_BLOCKS.  krow = the keep bitmap
+// row of row i's query block in the mask group (any valid row when
+// i >= Tq), looked up once per workgroup; only the key blocks are walked,
+// four at a time with their loads issued together (edges as scalar loads,
+// the lane's keep words as vector loads), instead of keymask32's scalar
+// walk over every (query block, key block) pair of the wave's rows.
+__device__ __forceinline__ uint64_t keymask64_blocks(const MaskDev& m, const uint64_t* krow, int i, int key0) {
+  const int kend = min(key0 + 64, m.Tk) - 1;
+  uint64_t bits = 0ull;
+  if (i >= m.Tq || key0 > kend) return 0ull;
+  const int ka = sld(m.col_kb + key0), kz = sld(m.col_kb + kend);
+  // 64 keys span at most 64 key blocks, so their keep bits lie in at most
+  // two consecutive words of the row.
+  const uint64_t w0 = krow[ka >> 6], w1 = krow[kz >> 6];
+  for (int k0 = ka; k0 <= kz; k0 += 4) {
+    int e[5];
+#pragma unroll
+    for (int x = 0; x < 5; ++x) e[x] = sld(m.k_edges + min(k0 + x, m.n_kb));
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int kb = k0 + x;
+      const uint64_t wd = ((kb >> 6) == (ka >> 6)) ? w0 : w1;
+      if (kb <= kz && ((wd >> (kb & 63)) & 1ull)) bits |= range_bits64(e[x] - key0, e[x + 1] - key0);
+    }
+  }
+  return bits;
+}
 // Allowed query rows among [row0, row0 + 64) for key j of a visited PARTIAL
 // tile of the dK/dV tiling, as a bitmask (bit r <-> row row0 + r): the same
 // predicate as keymask32, read along the key's column.  Rows >= Tq and keys
