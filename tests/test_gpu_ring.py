@@ -21,7 +21,7 @@ def _rank_rows(layout, N, C, rank):
     return M._ring_positions(spec, loc, "q")
 
 
-@pytest.mark.parametrize("d,n", [(128, 3), (64, 5), (128, 1)])
+@pytest.mark.parametrize("d,n", [(128, 3), (64, 5), (128, 1), (256, 4)])
 def test_lse_merge(d, n):
     """Merge of n bf16 partial outputs: rows with every part -inf, rows with some -inf parts."""
     import torch
@@ -47,13 +47,22 @@ def test_lse_merge(d, n):
     print(f"case merge d={d} n={n}", flush=True)
     mad.lse_merge(od, ld, o, lse)
     torch.cuda.synchronize()
-    _gpu.check_close("o", o.float().cpu().numpy(), ref_o, (1e-2, 5e-3))
+    _check_merged("o", o.float().cpu().numpy(), ref_o)
     _gpu.check_lse(lse.cpu().numpy(), ref_l)
     assert np.all(o.float().cpu().numpy()[3] == 0.0)
     # in place: the output aliases part 0
     mad.lse_merge(od, ld, od[0], ld[0])
     torch.cuda.synchronize()
-    _gpu.check_close("o in place", od[0].float().cpu().numpy(), ref_o, (1e-2, 5e-3))
+    _check_merged("o in place", od[0].float().cpu().numpy(), ref_o)
+
+
+def _check_merged(name, got, ref):
+    """The merged O is computed in fp32 and rounded once to bf16, which moves a value by at most
+    2^-8 of its magnitude (half an ulp of an 8-bit significand); 1e-4 covers the fp32 sums."""
+    err = np.abs(got - ref)
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-4
+    assert np.all(err <= bound), f"{name}: worst excess {float((err - bound).max()):.3e}"
+    _gpu.check_close(name, got, ref, (2e-2, 5e-3))
 
 
 def _ring_case(layout, N, C, rank, Hq, Hkv, d, seed, rows_check=None, full_bwd=True):
@@ -85,11 +94,12 @@ def _ring_case(layout, N, C, rank, Hq, Hkv, d, seed, rows_check=None, full_bwd=T
     return q, k, v, do, g_rows, scale, got, info
 
 
-@pytest.mark.parametrize("layout", ["contiguous", "headtail"])
-@pytest.mark.parametrize("rank", [0, 2, 3])
-def test_ring_small(layout, rank):
+@pytest.mark.parametrize("layout,rank,d", [("contiguous", 0, 128), ("contiguous", 2, 128), ("contiguous", 3, 128),
+                                           ("headtail", 0, 128), ("headtail", 2, 128), ("headtail", 3, 128),
+                                           ("headtail", 1, 256)])
+def test_ring_small(layout, rank, d):
     """Whole share of a 4-rank ring at chunk 256: merged O/LSE, accumulated dQ and the rank's dK/dV share."""
-    N, C, Hq, Hkv, d = 4, 256, 4, 2, 128
+    N, C, Hq, Hkv = 4, 256, 4, 2
     q, k, v, do, g_rows, scale, got, info = _ring_case(layout, N, C, rank, Hq, Hkv, d, seed=rank + 11)
     spec = M.MaskSpec("CAUSAL", N * C, N * C)
     O, L = A.attn_fwd(q, k, v, spec, scale, rows=g_rows)
