@@ -45,7 +45,7 @@ extern "C" {
 typedef enum {
   MAD_OK = 0,
   MAD_ERR_INVALID = 1,     /* bad argument: null pointer, size, range, plan/shape mismatch */
-  MAD_ERR_UNSUPPORTED = 2, /* valid but not built: head dim other than 64/128, alignment */
+  MAD_ERR_UNSUPPORTED = 2, /* valid but not built: head dim other than 64/128/256, alignment */
   MAD_ERR_HIP = 3,         /* a HIP runtime call failed (message holds the HIP error) */
   MAD_ERR_NOMEM = 4        /* host or device allocation for plan metadata failed */
 } mad_status;
@@ -257,7 +257,7 @@ void mad_plan_destroy(mad_plan* plan);
  * and head strides of q, k and v: {q_tok, q_head, k_tok, k_head, v_tok,
  * v_head}; the head dimension must be contiguous and every row 16-byte
  * aligned.  o, d_o, dq are packed [Tq, Hq, d]; dk, dv packed [Tk, Hkv, d];
- * lse is [Hq, Tq].  d must be 64 or 128; Hq % Hkv == 0; the plan must have
+ * lse is [Hq, Tq].  d must be 64, 128 or 256; Hq % Hkv == 0; the plan must have
  * been compiled for (Tq, Tk), uploaded, and have n_groups dividing Hq.
  * ------------------------------------------------------------------------- */
 
@@ -350,7 +350,7 @@ mad_status mad_block_mask(const void* q, const void* k, int32_t Tq, int32_t Tk, 
  *   o, lse     outputs in the same layouts; o may alias o_parts[t] and lse
  *              may alias lse_parts[t] (every element is read before it is
  *              written by the same thread).
- *   d          64 or 128.
+ *   d          64, 128 or 256.
  * Arithmetic in fp32, O rounded to bf16.  Runs on `stream`; allocates
  * nothing.  Invalid arguments return MAD_ERR_INVALID / MAD_ERR_UNSUPPORTED
  * before anything is launched.
@@ -379,7 +379,7 @@ mad_status mad_lse_merge(int32_t n_parts, const void* const* o_parts, const floa
  * outputs, the dQ accumulator, the backward workspace); the fwd / bwd calls
  * allocate nothing.
  *   layout     0 = contiguous, 1 = head-tail (chunk even).
- *   Hq, Hkv, d GQA heads (Hq % Hkv == 0) and head dim (64 or 128).
+ *   Hq, Hkv, d GQA heads (Hq % Hkv == 0) and head dim (64, 128 or 256).
  * Tensors (device, bf16, packed, 16-byte aligned): q, o, d_o, dq [chunk, Hq, d]
  * (the rank's local rows: contiguous -> global rows [rank*chunk, +chunk);
  * head-tail -> halves rank and 2*n_ranks-1-rank of chunk/2 rows each);

@@ -38,6 +38,10 @@ def flags():
         # directly, and the register allocator then keeps every kernel
         # spill-free (measured: forward 58.9 -> 22.7 ms at 32K causal)
         "-mllvm", "-amdgpu-mfma-vgpr-form",
+        # the D = 256 step loops are longer than the default full-unroll
+        # budget; partly unrolled, their operand arrays would be indexed at
+        # run time (D = 64 / 128 code is the same either way)
+        "-mllvm", "-pragma-unroll-threshold=1000000",
     ]
 
 

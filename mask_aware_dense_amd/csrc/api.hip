@@ -42,7 +42,7 @@ mad_status check_common(const char* fn, const mad_plan* p, const void* q, const 
   if (!p) return fail(MAD_ERR_INVALID, f + ": plan is NULL");
   if (Tq < 0 || Tk < 0 || Hq <= 0 || Hkv <= 0) return fail(MAD_ERR_INVALID, f + ": sizes must be Tq,Tk >= 0 and Hq,Hkv > 0");
   if (Hq % Hkv) return fail(MAD_ERR_INVALID, f + ": Hq must be a multiple of Hkv");
-  if (d != 64 && d != 128) return fail(MAD_ERR_UNSUPPORTED, f + ": head dim must be 64 or 128");
+  if (d != 64 && d != 128 && d != 256) return fail(MAD_ERR_UNSUPPORTED, f + ": head dim must be 64, 128 or 256");
   if (p->Tq != Tq || p->Tk != Tk)
     return fail(MAD_ERR_INVALID, f + ": plan was compiled for Tq=" + std::to_string(p->Tq) + ", Tk=" +
                                      std::to_string(p->Tk));
@@ -260,7 +260,8 @@ extern "C" mad_status mad_bwd_workspace_bytes(const mad_plan* p, int32_t Tq, int
   if (!bytes) return fail(MAD_ERR_INVALID, "mad_bwd_workspace_bytes: bytes is NULL");
   if (!p) return fail(MAD_ERR_INVALID, "mad_bwd_workspace_bytes: plan is NULL");
   if (Tq < 0 || Tk < 0 || Hq <= 0 || Hkv <= 0) return fail(MAD_ERR_INVALID, "mad_bwd_workspace_bytes: bad sizes");
-  if (d != 64 && d != 128) return fail(MAD_ERR_UNSUPPORTED, "mad_bwd_workspace_bytes: head dim must be 64 or 128");
+  if (d != 64 && d != 128 && d != 256)
+    return fail(MAD_ERR_UNSUPPORTED, "mad_bwd_workspace_bytes: head dim must be 64, 128 or 256");
   // -delta and -LSE/scale rows, each [Hq][Tq rounded up to 128] fp32; with
   // split dK/dV columns, fp32 dK and dV sums [Tk][Hkv][d] after them
   const size_t tq_pad = ((size_t)Tq + 127) / 128 * 128;

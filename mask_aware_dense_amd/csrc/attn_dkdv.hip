@@ -30,15 +30,23 @@
 
 namespace mad {
 
+// At D = 256 each workgroup accumulates one 128-column half of dK / dV
+// (blockIdx.y), with S and dP still taken over all of D: K, V and both full
+// accumulators would not fit in a lane's 512 registers.
 template <int D>
 __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
-  constexpr int BM = BM1, BN = BN1, NKS = D / 16, NDB = D / 32;
+  constexpr int DO = D == 256 ? 128 : D;  // dK / dV columns per workgroup
+  constexpr int BM = BM1, BN = BN1, NKS = D / 16, NDB = DO / 32;
+  const int c0 = D == 256 ? (int)blockIdx.y * DO : 0;  // first dK / dV column
   // D = 128: unpadded swizzled Q / dO tiles; D = 64: padded rows.
   constexpr int KIND = D == 128 ? TILE_SWZ : TILE_MIXED;
   constexpr int TILE = tile_elems<D, KIND>(), RS = tile_rs<D, KIND>();
   constexpr int S1 = 2 * NKS;   // phase-1 steps (block, k-step)
   constexpr int S2 = 4 * NDB;   // phase-2 steps (block, t2, d-block)
-  constexpr int EB = 16 / NKS;  // P / dS elements per stage-B step
+  // LDS operands are read RA steps ahead through rings of RA + 1 slots (one
+  // step at D = 256, where two would not leave registers to spare).
+  constexpr int RA = D == 256 ? 1 : 2, NR = RA + 1;
+  constexpr int EB = 16 / NKS >= 2 ? 16 / NKS : 2;  // P / dS elements per stage-B step (the first 16 / EB steps)
   constexpr int EC = 16 / (2 * NDB);  // P / dS elements per stage-C step
   __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];   // Q0 dO0 Q1 dO1
   __shared__ __attribute__((aligned(256))) float rowv[2][2 * BM];  // per buffer: -LSE/scale[64], -D[64]
@@ -246,33 +254,33 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
         }
       };
       // Phase-1 operands of step st: Q and dO rows b*32 + li, columns 16ks + 8hh.
-      bf16x8 opq[3], opd[3];
+      bf16x8 opq[NR], opd[NR];
       auto ld1 = [&](int st) {
         const int b = st / NKS, ks = st % NKS;
         if constexpr (KIND == TILE_SWZ) {
           const uint32_t off = srow.o[ks] + b * 32 * 256;
-          opq[st % 3] = ld16((const bf16*)((const char*)Qs + off));
-          opd[st % 3] = ld16((const bf16*)((const char*)Ds + off));
+          opq[st % NR] = ld16((const bf16*)((const char*)Qs + off));
+          opd[st % NR] = ld16((const bf16*)((const char*)Ds + off));
         } else {
           const int off = (b * 32 + li) * RS + 16 * ks + 8 * hh;
-          opq[st % 3] = ld16(Qs + off);
-          opd[st % 3] = ld16(Ds + off);
+          opq[st % NR] = ld16(Qs + off);
+          opd[st % NR] = ld16(Ds + off);
         }
       };
       // Phase-2 operands of step st: dO and Q read transposed; contraction
       // element e of half-wave hh is query row b*32 + 16 t2 + 8(e/4) + 4hh + e%4.
-      bf16x8 trd[3], trq[3];
+      bf16x8 trd[NR], trq[NR];
       auto ld2 = [&](int st) {
         const int b = st / (2 * NDB), t2 = (st / NDB) % 2, db = st % NDB;
         if constexpr (KIND == TILE_SWZ) {
           const uint32_t rb = (b * 32 + 16 * t2) * 256;
           const char *dc = (const char*)Ds, *qc = (const char*)Qs;
-          trd[st % 3] = ld_tr8((const bf16*)(dc + rb + str.o0[db]), (const bf16*)(dc + rb + str.o1[db]));
-          trq[st % 3] = ld_tr8((const bf16*)(qc + rb + str.o0[db]), (const bf16*)(qc + rb + str.o1[db]));
+          trd[st % NR] = ld_tr8((const bf16*)(dc + rb + str.o0[db]), (const bf16*)(dc + rb + str.o1[db]));
+          trq[st % NR] = ld_tr8((const bf16*)(qc + rb + str.o0[db]), (const bf16*)(qc + rb + str.o1[db]));
         } else {
-          const int qrow = b * 32 + 16 * t2 + 4 * hh + tr_row(lane), col = db * 32 + tr_col(lane);
-          trd[st % 3] = ld_tr8(Ds + qrow * RS + col, Ds + (qrow + 8) * RS + col);
-          trq[st % 3] = ld_tr8(Qs + qrow * RS + col, Qs + (qrow + 8) * RS + col);
+          const int qrow = b * 32 + 16 * t2 + 4 * hh + tr_row(lane), col = c0 + db * 32 + tr_col(lane);
+          trd[st % NR] = ld_tr8(Ds + qrow * RS + col, Ds + (qrow + 8) * RS + col);
+          trq[st % NR] = ld_tr8(Qs + qrow * RS + col, Qs + (qrow + 8) * RS + col);
         }
       };
       // P = exp2(c S) and dS = P dP for registers r, r + 1 of block b,
@@ -289,36 +297,37 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
       };
 
       init(0);
-      ld1(0);
-      ld1(1);
+#pragma unroll
+      for (int st = 0; st < RA; ++st) ld1(st);
       init(1);
       __builtin_amdgcn_sched_barrier(0);
       // Stage A.
 #pragma unroll
       for (int st = 0; st < NKS; ++st) {
-        ld1(st + 2);
-        sc[0] = mfma32(opq[st % 3], kf[st], sc[0]);
-        dp[0] = mfma32(opd[st % 3], vf[st], dp[0]);
+        ld1(st + RA);
+        sc[0] = mfma32(opq[st % NR], kf[st], sc[0]);
+        dp[0] = mfma32(opd[st % NR], vf[st], dp[0]);
         __builtin_amdgcn_sched_barrier(0);
       }
       // Stage B.
 #pragma unroll
       for (int st = NKS; st < S1; ++st) {
-        if (st + 2 < S1) ld1(st + 2);
-        else ld2(st + 2 - S1);
-        sc[1] = mfma32(opq[st % 3], kf[st - NKS], sc[1]);
-        dp[1] = mfma32(opd[st % 3], vf[st - NKS], dp[1]);
+        if (st + RA < S1) ld1(st + RA);
+        else ld2(st + RA - S1);
+        sc[1] = mfma32(opq[st % NR], kf[st - NKS], sc[1]);
+        dp[1] = mfma32(opd[st % NR], vf[st - NKS], dp[1]);
 #pragma unroll
-        for (int x = 0; x < EB; x += 2) pds(0, (st - NKS) * EB + x);
+        for (int x = 0; x < EB; x += 2)
+          if ((st - NKS) * EB + x < 16) pds(0, (st - NKS) * EB + x);
         __builtin_amdgcn_sched_barrier(0);
       }
       // Stages C and D.
 #pragma unroll
       for (int st = 0; st < S2; ++st) {
-        if (st + 2 < S2) ld2(st + 2);
+        if (st + RA < S2) ld2(st + RA);
         const int b = st / (2 * NDB), t2 = (st / NDB) % 2, db = st % NDB;
-        dva[db] = mfma32(pa[b][t2], trd[st % 3], dva[db]);
-        dka[db] = mfma32(sa[b][t2], trq[st % 3], dka[db]);
+        dva[db] = mfma32(pa[b][t2], trd[st % NR], dva[db]);
+        dka[db] = mfma32(sa[b][t2], trq[st % NR], dka[db]);
         if (st < 2 * NDB) {
 #pragma unroll
           for (int x = 0; x < EC; x += 2) pds(1, st * EC + x);
@@ -338,7 +347,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
         for (int r = 0; r < 16; ++r) {
           const int kk = kt * BN + w * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
           if (kk < P.Tk) {
-            const int64_t off = ((int64_t)kk * P.Hkv + g) * D + db * 32 + li;
+            const int64_t off = ((int64_t)kk * P.Hkv + g) * D + c0 + db * 32 + li;
             unsafeAtomicAdd(P.dk_acc + off, dka[db][r] * P.scale);
             unsafeAtomicAdd(P.dv_acc + off, dva[db][r]);
           }
@@ -352,7 +361,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
     for (int r = 0; r < 16; ++r) {
       const int kk = kt * BN + w * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
       if (kk < P.Tk) {
-        const int64_t off = ((int64_t)kk * P.Hkv + g) * D + db * 32 + li;
+        const int64_t off = ((int64_t)kk * P.Hkv + g) * D + c0 + db * 32 + li;
         P.dk[off] = (bf16)(dka[db][r] * P.scale);
         P.dv[off] = (bf16)dva[db][r];
       }
@@ -383,6 +392,7 @@ hipError_t launch_dkdv(const AttnParams& P, int D, int n_items, hipStream_t stre
   const int nb = (int)std::min<int64_t>((n4 + 255) / 256, 4096);
   if (S > 1 && n4 > 0) hipLaunchKernelGGL(zero2_kernel, dim3(nb), dim3(256), 0, stream, P.dk_acc, P.dv_acc, n4);
   if (D == 128) hipLaunchKernelGGL(dkdv_kernel<128>, dim3(n_items * S), dim3(256), 0, stream, P);
+  else if (D == 256) hipLaunchKernelGGL(dkdv_kernel<256>, dim3(n_items * S, 2), dim3(256), 0, stream, P);
   else hipLaunchKernelGGL(dkdv_kernel<64>, dim3(n_items * S), dim3(256), 0, stream, P);
   if (S > 1 && n4 > 0)
     hipLaunchKernelGGL(round2_kernel, dim3(nb), dim3(256), 0, stream, P.dk_acc, P.dv_acc, P.dk, P.dv, n4);

@@ -347,11 +347,14 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
   }
 }
 
-constexpr int FWD_NB = 1;  // 4 waves of 32 rows: 220 registers, two waves per SIMD
+// 4 waves of 32 rows: 220 registers at D = 128, two waves per SIMD (one at
+// D = 256, whose K / V double buffer also fills 141 KB of LDS).
+constexpr int FWD_NB = 1;
 
 hipError_t launch_fwd(const AttnParams& P, int D, int n_items, hipStream_t stream) {
   if (n_items <= 0) return hipSuccess;
   if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, FWD_NB>), dim3(n_items), dim3(256 / FWD_NB), 0, stream, P);
+  else if (D == 256) hipLaunchKernelGGL((fwd_kernel<256, 1>), dim3(n_items), dim3(256), 0, stream, P);
   else hipLaunchKernelGGL((fwd_kernel<64, FWD_NB>), dim3(n_items), dim3(256 / FWD_NB), 0, stream, P);
   return hipGetLastError();
 }

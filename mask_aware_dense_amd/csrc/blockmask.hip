@@ -20,6 +20,8 @@
 #include <algorithm>
 #include <string>
 
+#include <type_traits>
+
 #include "kernel_common.hpp"
 
 namespace mad {
@@ -150,7 +152,8 @@ extern "C" mad_status mad_block_mask_workspace_bytes(int32_t n_groups, int32_t H
   clear_error();
   if (!bytes) return fail(MAD_ERR_INVALID, "mad_block_mask_workspace_bytes: bytes is NULL");
   if (n_groups <= 0 || Hkv <= 0 || n_qb <= 0 || n_kb <= 0) return fail(MAD_ERR_INVALID, "mad_block_mask_workspace_bytes: bad sizes");
-  if (d != 64 && d != 128) return fail(MAD_ERR_UNSUPPORTED, "mad_block_mask_workspace_bytes: head dim must be 64 or 128");
+  if (d != 64 && d != 128 && d != 256)
+    return fail(MAD_ERR_UNSUPPORTED, "mad_block_mask_workspace_bytes: head dim must be 64, 128 or 256");
   const size_t a = ((size_t)n_groups * n_qb * d * 4 + 255) / 256 * 256;
   *bytes = a + (size_t)Hkv * n_kb * d * 4;
   return MAD_OK;
@@ -164,7 +167,7 @@ extern "C" mad_status mad_block_mask(const void* q, const void* k, int32_t Tq, i
   clear_error();
   const std::string f = "mad_block_mask";
   if (Tq <= 0 || Tk <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return fail(MAD_ERR_INVALID, f + ": bad sizes");
-  if (d != 64 && d != 128) return fail(MAD_ERR_UNSUPPORTED, f + ": head dim must be 64 or 128");
+  if (d != 64 && d != 128 && d != 256) return fail(MAD_ERR_UNSUPPORTED, f + ": head dim must be 64, 128 or 256");
   if (n_groups <= 0 || Hq % n_groups || n_groups % Hkv)
     return fail(MAD_ERR_INVALID, f + ": n_groups must divide Hq and be a multiple of Hkv (a group's heads share one KV head)");
   if (n_qb <= 0 || n_kb <= 0 || n_qb > Tq || n_kb > Tk) return fail(MAD_ERR_INVALID, f + ": bad block counts");
@@ -183,21 +186,18 @@ extern "C" mad_status mad_block_mask(const void* q, const void* k, int32_t Tq, i
   const int kkeep = std::max(1, n_kb - (int)(((int64_t)sparsity_pct * n_kb) / 100));
   const int nw = (n_kb + 63) / 64;
   const int64_t q_tok = (int64_t)Hq * d, k_tok = (int64_t)Hkv * d;
-  if (d == 128) {
-    hipLaunchKernelGGL(pool_kernel<128>, dim3(n_groups * n_qb), dim3(256), 0, stream, (const bf16*)q, q_tok, (int64_t)d,
+  auto run = [&](auto dtag) {
+    constexpr int DD = decltype(dtag)::value;
+    hipLaunchKernelGGL(pool_kernel<DD>, dim3(n_groups * n_qb), dim3(256), 0, stream, (const bf16*)q, q_tok, (int64_t)d,
                        q_edges, n_qb, Hq / n_groups, Tq, qp);
-    hipLaunchKernelGGL(pool_kernel<128>, dim3(Hkv * n_kb), dim3(256), 0, stream, (const bf16*)k, k_tok, (int64_t)d,
+    hipLaunchKernelGGL(pool_kernel<DD>, dim3(Hkv * n_kb), dim3(256), 0, stream, (const bf16*)k, k_tok, (int64_t)d,
                        k_edges, n_kb, 1, Tk, kp);
-    hipLaunchKernelGGL(score_topk_kernel<128>, dim3(n_groups * n_qb), dim3(256), 0, stream, qp, kp, n_qb, n_kb,
+    hipLaunchKernelGGL(score_topk_kernel<DD>, dim3(n_groups * n_qb), dim3(256), 0, stream, qp, kp, n_qb, n_kb,
                        n_groups / Hkv, kkeep, scale, keep, nw, scores);
-  } else {
-    hipLaunchKernelGGL(pool_kernel<64>, dim3(n_groups * n_qb), dim3(256), 0, stream, (const bf16*)q, q_tok, (int64_t)d,
-                       q_edges, n_qb, Hq / n_groups, Tq, qp);
-    hipLaunchKernelGGL(pool_kernel<64>, dim3(Hkv * n_kb), dim3(256), 0, stream, (const bf16*)k, k_tok, (int64_t)d,
-                       k_edges, n_kb, 1, Tk, kp);
-    hipLaunchKernelGGL(score_topk_kernel<64>, dim3(n_groups * n_qb), dim3(256), 0, stream, qp, kp, n_qb, n_kb,
-                       n_groups / Hkv, kkeep, scale, keep, nw, scores);
-  }
+  };
+  if (d == 128) run(std::integral_constant<int, 128>{});
+  else if (d == 256) run(std::integral_constant<int, 256>{});
+  else run(std::integral_constant<int, 64>{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hipf("mad_block_mask: launch", e);
   return MAD_OK;

@@ -114,11 +114,14 @@ __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1)
 // SQ_LDS_BANK_CONFLICT counter):
 //   ROWS  - 16-byte row reads (MFMA operand rows): 8 lanes per pass read the
 //           same column of 8 consecutive rows; conflict-free when the stride
-//           is 4 mod 8 dwords (272 B for D=128, 144 B for D=64).
+//           is 4 mod 8 dwords (528 B for D=256, 272 B for D=128, 144 B for
+//           D=64).
 //   TR    - transposed reads (ds_read_b64_tr_b16): 32 lanes per pass read
 //           64 bytes of each of 4 consecutive rows; conflict-free when the
-//           stride is 16 mod 32 dwords (320 B for D=128, 192 B for D=64).
-//   MIXED - both; 304 B (D=128) / 144 B (D=64) keeps row reads conflict-free.
+//           stride is 16 mod 32 dwords (576 B for D=256, 320 B for D=128,
+//           192 B for D=64).
+//   MIXED - both; 560 B (D=256), 304 B (D=128), 144 B (D=64) keep row reads
+//           conflict-free.
 //           A pure-read probe shows two-way conflicts on transposed reads at
 //           this stride, but in the kernels' access order (a wave's 32 lanes
 //           reading 4 rows of one 64-byte column block) the counter stays at
@@ -136,9 +139,11 @@ __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1)
 enum TileKind { TILE_ROWS = 0, TILE_TR = 1, TILE_MIXED = 2, TILE_SWZ = 3 };
 template <int D, int KIND>
 constexpr int tile_rs() {
+  static_assert(D == 64 || D == 128 || D == 256, "head dim 64, 128 or 256");
   static_assert(KIND != TILE_SWZ || D == 128, "the swizzled tile is for D = 128");
-  return D == 128 ? (KIND == TILE_ROWS ? 136 : KIND == TILE_TR ? 160 : KIND == TILE_SWZ ? 128 : 152)
-                  : (KIND == TILE_TR ? 96 : 72);
+  return D == 256   ? (KIND == TILE_ROWS ? 264 : KIND == TILE_TR ? 288 : 280)
+         : D == 128 ? (KIND == TILE_ROWS ? 136 : KIND == TILE_TR ? 160 : KIND == TILE_SWZ ? 128 : 152)
+                    : (KIND == TILE_TR ? 96 : 72);
 }
 // Chunk permutation of storage row p of a SWZ tile.
 __device__ __forceinline__ int swz_row(int p) { return ((p & 3) << 2) | ((p >> 2) & 3); }

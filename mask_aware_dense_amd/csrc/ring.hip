@@ -110,6 +110,7 @@ hipError_t launch_merge(const MergeArgs& A, int d, hipStream_t s) {
   if (threads == 0) return hipSuccess;
   const int nb = (int)((threads + 255) / 256);
   if (d == 128) hipLaunchKernelGGL(lse_merge_kernel<128>, dim3(nb), dim3(256), 0, s, A);
+  else if (d == 256) hipLaunchKernelGGL(lse_merge_kernel<256>, dim3(nb), dim3(256), 0, s, A);
   else hipLaunchKernelGGL(lse_merge_kernel<64>, dim3(nb), dim3(256), 0, s, A);
   return hipGetLastError();
 }
@@ -125,7 +126,7 @@ extern "C" mad_status mad_lse_merge(int32_t n_parts, const void* const* o_parts,
   if (n_parts < 1 || n_parts > MAX_PARTS)
     return fail(MAD_ERR_INVALID, "mad_lse_merge: n_parts must be in 1.." + std::to_string(MAX_PARTS));
   if (Tq < 0 || Hq <= 0) return fail(MAD_ERR_INVALID, "mad_lse_merge: sizes must be Tq >= 0 and Hq > 0");
-  if (d != 64 && d != 128) return fail(MAD_ERR_UNSUPPORTED, "mad_lse_merge: head dim must be 64 or 128");
+  if (d != 64 && d != 128 && d != 256) return fail(MAD_ERR_UNSUPPORTED, "mad_lse_merge: head dim must be 64, 128 or 256");
   if (!o_parts || !lse_parts) return fail(MAD_ERR_INVALID, "mad_lse_merge: part arrays must not be NULL");
   if (Tq == 0) return MAD_OK;
   if (!o || !lse) return fail(MAD_ERR_INVALID, "mad_lse_merge: o/lse must not be NULL");
@@ -243,7 +244,8 @@ extern "C" mad_status mad_ring_create(int32_t layout, int32_t n_ranks, int32_t c
   if ((int64_t)chunk * n_ranks > INT32_MAX) return fail(MAD_ERR_UNSUPPORTED, "mad_ring_create: sequence too long");
   if (rank < 0 || rank >= n_ranks) return fail(MAD_ERR_INVALID, "mad_ring_create: rank out of range");
   if (Hq <= 0 || Hkv <= 0 || Hq % Hkv) return fail(MAD_ERR_INVALID, "mad_ring_create: Hq must be a positive multiple of Hkv");
-  if (d != 64 && d != 128) return fail(MAD_ERR_UNSUPPORTED, "mad_ring_create: head dim must be 64 or 128");
+  if (d != 64 && d != 128 && d != 256)
+    return fail(MAD_ERR_UNSUPPORTED, "mad_ring_create: head dim must be 64, 128 or 256");
   mad_ring* r = new mad_ring();
   r->layout = layout;
   r->N = n_ranks;

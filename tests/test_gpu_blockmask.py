@@ -47,6 +47,7 @@ def _run(q, k, qe, ke, G, pct, scale):
     (4096, 8, 2, 2, 128, 128, 50),
     (300, 2, 1, 1, 64, 32, 100),      # k = 1
     (300, 2, 1, 2, 64, 32, 0),        # keep all
+    (1200, 4, 2, 2, 256, 64, 50),     # head dim 256
 ])
 def test_block_mask_matches_oracle(T, Hq, Hkv, G, d, b, pct):
     q, k, _ = qkv(T + pct, T, T, Hq, Hkv, d)

@@ -61,6 +61,14 @@ def test_causal_32k_gqa_64_8():
     _check_bwd_invariants(got, do, np.ones((32768, 64), bool), 8)
 
 
+def test_causal_16k_gqa_64_8_d256():
+    """Head dim 256 at a full size: CAUSAL, T=16384, GQA 64:8 (dQ, dK, dV in two column halves)."""
+    spec = M.MaskSpec("CAUSAL", 16384, 16384)
+    q, k, v, do, scale, got = _full_run(spec, 64, 8, 256, seed=4)
+    _check_sampled(spec, q, k, v, do, scale, got, n_rows=24, heads=[0, 9, 40, 63])
+    _check_bwd_invariants(got, do, np.ones((16384, 64), bool), 8)
+
+
 def test_global_sliding_32k_gqa_64_8():
     """GLOBAL_SLIDING at the suite's shape (256 global keys, 2K window): its two global key tiles
     hold most of the dK/dV items, so their columns are cut between workgroups (fp32 sums)."""

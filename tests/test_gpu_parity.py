@@ -49,7 +49,7 @@ def test_tiny_reference_config(pattern):
     _run_case(spec, _plan_for(spec), 4, 4, 64, seed=0)
 
 
-@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("d", [128, 64, 256])
 @pytest.mark.parametrize("idx", range(len(M.STATIC_PATTERNS)))
 def test_static_patterns_small(idx, d):
     T = 1000 + 37 * idx  # ragged: never a multiple of the 128 / 64 tile sizes
@@ -58,7 +58,7 @@ def test_static_patterns_small(idx, d):
 
 
 @pytest.mark.parametrize("bottom_right", [False, True])
-@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("d", [128, 64, 256])
 def test_varlen_cross_attention(bottom_right, d):
     """A batch of packed sequences with different query and key lengths (causal; bottom-right
     alignment leaves the first Lq - Lk rows of a sequence with no key: O = 0, LSE = -inf)."""
@@ -98,6 +98,16 @@ def test_block_sparse(b, variable, pct, heads):
     _run_case(spec, plan, Hq, Hkv, 128, seed=7)
 
 
+@pytest.mark.parametrize("b,variable", [(64, False), (0, True)])
+@pytest.mark.parametrize("heads", [(8, 8), (8, 2)], ids=["mha", "gqa"])
+def test_block_sparse_d256(b, variable, heads):
+    """Head dim 256 (dQ, dK and dV in two 128-column halves) under mixed-strip block masks."""
+    Hq, Hkv = heads
+    T = 1536 if not variable else 1333
+    plan, spec = _sparse(T, b, Hkv, 50, seed=b + Hkv + 256, variable=variable)
+    _run_case(spec, plan, Hq, Hkv, 256, seed=9)
+
+
 def test_block_sparse_ragged_uniform():
     plan, spec = _sparse(1000, 64, 2, 50, seed=3, variable=False)  # last block of 40
     _run_case(spec, plan, 4, 2, 64, seed=8)
@@ -113,11 +123,17 @@ def test_ring_step(layout, rs):
     _run_case(spec, _plan_for(spec), 8, 1, 128, seed=20 + r * 12 + s)
 
 
+def test_ring_step_d256():
+    spec = M.MaskSpec("RING_STEP", 1024, 1024, layout="headtail", n_ranks=12, rank=5, source=9)
+    _run_case(spec, _plan_for(spec), 8, 2, 256, seed=77)
+
+
+@pytest.mark.parametrize("d", [64, 256])
 @pytest.mark.parametrize("T", [1, 17, 65, 129])
-def test_tiny_and_ragged(T):
+def test_tiny_and_ragged(T, d):
     for pat in ("CAUSAL", "FULL"):
         spec = M.MaskSpec(pat, T, T)
-        _run_case(spec, _plan_for(spec), 2, 1, 64, seed=T)
+        _run_case(spec, _plan_for(spec), 2, 1, d, seed=T)
 
 
 def test_empty_key_range_gives_zero_and_neg_inf():
