@@ -227,6 +227,15 @@ def suite_workloads(seed):
     ]:
         out.append((f"{pattern} 32K GQA 64:8", static(pattern, **kw)))
 
+    def head_dim(pattern, d):
+        def build(mad):
+            return mad.mask_compile(mad.mask_slices(pattern, T), T, T), T, T, 64, 8, d, {
+                "mask": pattern, "seq_len": T}
+        return build
+
+    for d in (64, 256):
+        out.append((f"CAUSAL 32K GQA 64:8 d={d}", head_dim("CAUSAL", d)))
+
     def varlen_continuation():
         # a batch of the same 32K of documents as keys; each sequence's queries are the
         # last half of its tokens (a chunk that continues a cached prefix), causal,
