@@ -359,6 +359,20 @@ __device__ __forceinline__ uint32_t keymask32(const MaskDev& m, int32_t aux, int
     if (key0 <= kend && row_lo <= rhi) {
       const int qa = sld(m.row_qb + row_lo), qz = sld(m.row_qb + rhi);
       const int ka = sld(m.col_kb + key0), kz = sld(m.col_kb + kend);
+      if (qz - qa <= 1 && kz - ka <= 1) {
+        // At most two query blocks and two key blocks (always, for blocks of
+        // 32 or more): every keep word and edge is loaded in one batch.
+        const uint64_t* ra = m.keep + ((size_t)grp * m.n_qb + qa) * m.nw;
+        const uint64_t* rz = m.keep + ((size_t)grp * m.n_qb + qz) * m.nw;
+        const uint64_t waa = sld(ra + (ka >> 6)), waz = sld(ra + (kz >> 6));
+        const uint64_t wza = sld(rz + (ka >> 6)), wzz = sld(rz + (kz >> 6));
+        const int e0 = sld(m.k_edges + ka), e1 = sld(m.k_edges + ka + 1), e2 = sld(m.k_edges + kz + 1);
+        const int qsplit = sld(m.q_edges + qa + 1);  // first row of block qa + 1
+        const bool in_a = i < qsplit;                 // this lane's row is in block qa (else in qz)
+        const uint64_t w0 = in_a ? waa : wza, w1 = in_a ? waz : wzz;
+        if ((w0 >> (ka & 63)) & 1ull) bits |= range_bits(e0 - key0, e1 - key0);
+        if (kz > ka && ((w1 >> (kz & 63)) & 1ull)) bits |= range_bits(e1 - key0, e2 - key0);
+      } else
       for (int qb = qa; qb <= qz; ++qb) {
         const uint64_t* krow = m.keep + ((size_t)grp * m.n_qb + qb) * m.nw;
         uint32_t kbits = 0u;  // kept keys of query block qb in this 32-key range
