@@ -236,6 +236,26 @@ def suite_workloads(seed):
     for d in (64, 256):
         out.append((f"CAUSAL 32K GQA 64:8 d={d}", head_dim("CAUSAL", d)))
 
+    # the regular masks at the other totals and head layouts the workloads name
+    def sized(pattern, T_, Hq, Hkv, **kw):
+        def build(mad):
+            kw2 = dict(kw)
+            if "doc_lens" in kw2:
+                kw2["doc_lens"] = [int(x) for x in doc_lengths(seed, T_)]
+            sl = mad.mask_slices(pattern, T_, **kw2)
+            return mad.mask_compile(sl, T_, T_), T_, T_, Hq, Hkv, 128, {
+                "mask": pattern, "seq_len": T_, **({"window": kw["window"]} if "window" in kw else {}),
+                **({"doc_lens": f"{len(kw2['doc_lens'])} documents"} if "doc_lens" in kw2 else {})}
+        return build
+
+    for pattern, T_, Hq, Hkv, kw in [
+        ("CAUSAL", 8192, 64, 8, {}), ("CAUSAL", 49152, 64, 8, {}), ("CAUSAL", 32768, 64, 64, {}),
+        ("FULL", 16384, 64, 64, {}), ("SLIDING_WINDOW", 49152, 64, 64, {"window": 4096}),
+        ("CAUSAL_DOCUMENT", 49152, 64, 8, {"doc_lens": True}), ("FULL_DOCUMENT", 16384, 64, 64, {"doc_lens": True}),
+    ]:
+        heads = "MHA 64:64" if Hq == Hkv else f"GQA {Hq}:{Hkv}"
+        out.append((f"{pattern} {T_ // 1024}K {heads}", sized(pattern, T_, Hq, Hkv, **kw)))
+
     def varlen_continuation():
         # a batch of the same 32K of documents as keys; each sequence's queries are the
         # last half of its tokens (a chunk that continues a cached prefix), causal,
