@@ -74,15 +74,11 @@ __global__ __launch_bounds__(256) void delta_kernel(const AttnParams P) {
 // three-slot register rings, each step closed by a scheduling fence.  Masked
 // scores start at -inf, so their P is exactly 0 with no per-element test.
 // ---------------------------------------------------------------------------
-// Two workgroups per CU at D = 64 / 128.  At D = 256 the Q / dO operands
-// alone take 128 registers per lane, so each workgroup accumulates one
-// 128-column half of dQ (blockIdx.y; S and dP still run over all of D), at
-// one workgroup per CU.
+// Two workgroups per CU at D = 64 / 128; one at D = 256, where the Q / dO
+// operands and the dQ accumulator take 256 registers per lane (421 in all).
 template <int D>
 __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void dq_kernel(const AttnParams P) {
-  constexpr int DO = D == 256 ? 128 : D;  // dQ columns per workgroup
-  constexpr int BM = BM0, BN = BN0, NKS = D / 16, NDB = DO / 32;
-  const int c0 = D == 256 ? (int)blockIdx.y * DO : 0;  // first dQ column
+  constexpr int BM = BM0, BN = BN0, NKS = D / 16, NDB = D / 32;
   constexpr int KRS = tile_rs<D, TILE_MIXED>(), KT = tile_elems<D, TILE_MIXED>();
   constexpr int VRS = tile_rs<D, TILE_ROWS>(), VT = tile_elems<D, TILE_ROWS>();
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * (KT + VT)];  // K0 V0 K1 V1
@@ -190,7 +186,7 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void dq_kernel(const AttnPar
     bf16x8 trk[3];
     auto ld2 = [&](int st) {
       const int kb = st / (2 * NDB), t2 = (st / NDB) % 2, db = st % NDB;
-      const int krow = kb * 32 + 16 * t2 + 4 * hh + tr_row(lane), kcol = c0 + db * 32 + tr_col(lane);
+      const int krow = kb * 32 + 16 * t2 + 4 * hh + tr_row(lane), kcol = db * 32 + tr_col(lane);
       trk[st % 3] = ld_tr8(Ks + krow * KRS + kcol, Ks + (krow + 8) * KRS + kcol);
     };
     bf16x8 sb[2][2];  // dS^T as B operands, [kb][t2]
@@ -235,10 +231,10 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void dq_kernel(const AttnPar
     }
   }
 
-  // dQ^T: lane holds query row `row`, column d = c0 + db*32 + 8(r/4) + 4hh + r%4.
+  // dQ^T: lane holds query row `row`, column d = db*32 + 8(r/4) + 4hh + r%4.
   if (row < P.Tq && P.dq_acc) {
     // Accumulating form (one call per key chunk): each element has one owner lane.
-    float* dst = P.dq_acc + ((int64_t)row * P.Hq + h) * D + c0;
+    float* dst = P.dq_acc + ((int64_t)row * P.Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -252,7 +248,7 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void dq_kernel(const AttnPar
         *p4 = v4;
       }
   } else if (row < P.Tq) {
-    bf16* dst = P.dq + ((int64_t)row * P.Hq + h) * D + c0;
+    bf16* dst = P.dq + ((int64_t)row * P.Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -285,7 +281,7 @@ hipError_t launch_bwd(const AttnParams& Pq, const AttnParams& Pkv, int D, int nq
   }
   if ((phases & MAD_BWD_DQ) && nq_items > 0) {
     if (D == 128) hipLaunchKernelGGL(dq_kernel<128>, dim3(nq_items), dim3(256), 0, stream, Pq);
-    else if (D == 256) hipLaunchKernelGGL(dq_kernel<256>, dim3(nq_items, 2), dim3(256), 0, stream, Pq);
+    else if (D == 256) hipLaunchKernelGGL(dq_kernel<256>, dim3(nq_items), dim3(256), 0, stream, Pq);
     else hipLaunchKernelGGL(dq_kernel<64>, dim3(nq_items), dim3(256), 0, stream, Pq);
   }
   return hipGetLastError();
