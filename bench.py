@@ -572,7 +572,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
-                          "detail": "no collectives or sharding are built; see the design notes on sharding"}))
+                          "detail": "no collectives or sharding are built: the kernels run one GPU's share (whole heads or one ring step) and value is that GPU's throughput"}))
         sys.exit(2)
     import torch
     if args.copy_calibration:
