@@ -15,7 +15,7 @@ blockwise blocks of 2K, Block Causal Document block 1024 (appendix A.4.1
 "Block causal document").  Block-sparse: appendix A.2 (block partition,
 scores, top-k per query block).
 
-Readings where the pages are silent (each also listed in the design notes):
+Readings where the pages are silent (the library takes the same ones):
   * sliding window W counts the key itself: i-W < j <= i
   * Prefix LM prefix P = floor(T/4), bidirectional inside the prefix
   * Shared Question answers split the rest equally, the last takes the
