@@ -192,6 +192,7 @@ extern "C" mad_status mad_plan_upload(mad_plan* p, hipStream_t stream) {
     d.order = (const int32_t*)(base + off_t[w][3]);
     d.nmajor = w == 0 ? t.nqt : t.nkt;
     d.nminor = w == 0 ? t.nkt : t.nqt;
+    d.BN = t.BN;
   }
   MaskDev& m = p->mdev;
   m.mode = p->mode;

@@ -33,10 +33,13 @@ namespace mad {
 // At D = 256 each workgroup accumulates one 128-column half of dK / dV
 // (blockIdx.y), with S and dP still taken over all of D: K, V and both full
 // accumulators would not fit in a lane's 512 registers.
-template <int D>
-__global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
+// NW waves of 32 keys: a 128-key tile (NW = 4, one workgroup per CU) or,
+// for block-sparse plans of 64-token key blocks, a 64-key tile (NW = 2, two
+// workgroups per CU).
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void dkdv_kernel(const AttnParams P) {
   constexpr int DO = D == 256 ? 128 : D;  // dK / dV columns per workgroup
-  constexpr int BM = BM1, BN = BN1, NKS = D / 16, NDB = DO / 32;
+  constexpr int BM = BM1, BN = 32 * NW, NKS = D / 16, NDB = DO / 32;
   const int c0 = D == 256 ? (int)blockIdx.y * DO : 0;  // first dK / dV column
   // D = 128: unpadded swizzled Q / dO tiles; D = 64: padded rows.
   constexpr int KIND = D == 128 ? TILE_SWZ : TILE_MIXED;
@@ -44,8 +47,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
   constexpr int S1 = 2 * NKS;   // phase-1 steps (block, k-step)
   constexpr int S2 = 4 * NDB;   // phase-2 steps (block, t2, d-block)
   // LDS operands are read RA steps ahead through rings of RA + 1 slots (one
-  // step at D = 256, where two would not leave registers to spare).
-  constexpr int RA = D == 256 ? 1 : 2, NR = RA + 1;
+  // step at D = 256, where two would not leave registers to spare, and none
+  // for the two-wave D = 256 form).
+  constexpr int RA = D == 256 ? (NW == 2 ? 0 : 1) : 2, NR = RA + 1;
   constexpr int EB = 16 / NKS >= 2 ? 16 / NKS : 2;  // P / dS elements per stage-B step (the first 16 / EB steps)
   constexpr int EC = 16 / (2 * NDB);  // P / dS elements per stage-C step
   __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];   // Q0 dO0 Q1 dO1
@@ -172,7 +176,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const AttnParams P) {
     return cu;
   };
   const uint32_t smem_lds = lds_addr(smem), rowv_lds = lds_addr(&rowv[0][0]);
-  TileLoader<D, KIND, 4, false> qload, dload;
+  TileLoader<D, KIND, NW, false> qload, dload;
   SwzRows srow;
   SwzTr str;
   if constexpr (KIND == TILE_SWZ) {
@@ -391,9 +395,17 @@ hipError_t launch_dkdv(const AttnParams& P, int D, int n_items, hipStream_t stre
   const int64_t n4 = (int64_t)P.Tk * P.Hkv * D / 4;  // D is a multiple of 4
   const int nb = (int)std::min<int64_t>((n4 + 255) / 256, 4096);
   if (S > 1 && n4 > 0) hipLaunchKernelGGL(zero2_kernel, dim3(nb), dim3(256), 0, stream, P.dk_acc, P.dv_acc, n4);
-  if (D == 128) hipLaunchKernelGGL(dkdv_kernel<128>, dim3(n_items * S), dim3(256), 0, stream, P);
-  else if (D == 256) hipLaunchKernelGGL(dkdv_kernel<256>, dim3(n_items * S, 2), dim3(256), 0, stream, P);
-  else hipLaunchKernelGGL(dkdv_kernel<64>, dim3(n_items * S), dim3(256), 0, stream, P);
+  const dim3 grid(n_items * S, D == 256 ? 2 : 1);
+  auto run = [&](auto k, int nw) { hipLaunchKernelGGL(k, grid, dim3(64 * nw), 0, stream, P); };
+  if (P.t.BN == BN1_FINE) {
+    if (D == 128) run(dkdv_kernel<128, 2>, 2);
+    else if (D == 256) run(dkdv_kernel<256, 2>, 2);
+    else run(dkdv_kernel<64, 2>, 2);
+  } else {
+    if (D == 128) run(dkdv_kernel<128, 4>, 4);
+    else if (D == 256) run(dkdv_kernel<256, 4>, 4);
+    else run(dkdv_kernel<64, 4>, 4);
+  }
   if (S > 1 && n4 > 0)
     hipLaunchKernelGGL(round2_kernel, dim3(nb), dim3(256), 0, stream, P.dk_acc, P.dv_acc, P.dk, P.dv, n4);
   return hipGetLastError();

@@ -263,19 +263,27 @@ __device__ __forceinline__ int tile_row(int p, bool perm) { return perm ? ((p & 
 template <int D, int KIND, int NW, bool PERM>
 struct TileLoader {
   static constexpr int SPR = tile_rs<D, KIND>() / 8, CPR = D / 8, NI = (SPR + NW - 1) / NW;
-  uint32_t off[NI];  // byte offset of this lane's source chunk from the tile's first row
+  // Byte offset of this lane's source chunk from the tile's first row, per
+  // instruction: kept in registers for up to 9 instructions per wave, else
+  // (two waves loading 512-byte rows) recomputed at each issue, where 18
+  // registers per tile would not fit beside the kernel's operands.
+  static constexpr bool KEEP = NI <= 9;
+  uint32_t off[KEEP ? NI : 1];
 
   // Tensor chunk held by storage slot (row p, chunk c); pad slots repeat chunk 0.
   static __device__ __forceinline__ int src_chunk(int p, int c) {
     return c >= CPR ? 0 : (KIND == TILE_SWZ ? c ^ swz_row(p) : c);
   }
 
+  static __device__ __forceinline__ uint32_t offset(int i, int64_t tok, int w, int lane) {
+    const int s = (i * NW + w) * 64 + lane;
+    const int p = s / SPR, c = s % SPR;
+    return (uint32_t)(((int64_t)tile_row(p, PERM) * tok + src_chunk(p, c) * 8) * 2);
+  }
   __device__ __forceinline__ void init(int64_t tok, int w, int lane) {
+    if constexpr (KEEP) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int s = (i * NW + w) * 64 + lane;
-      const int p = s / SPR, c = s % SPR;
-      off[i] = (uint32_t)(((int64_t)tile_row(p, PERM) * tok + src_chunk(p, c) * 8) * 2);
+      for (int i = 0; i < NI; ++i) off[i] = offset(i, tok, w, lane);
     }
   }
   // lds: LDS byte address of the tile image; g: the tensor's head; tok: its
@@ -288,7 +296,14 @@ struct TileLoader {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int ii = i * NW + w;
-        if ((i + 1) * NW <= SPR || ii < SPR) g2lds16(base, off[i], lds + ii * 1024);
+        if ((i + 1) * NW <= SPR || ii < SPR) {
+          if constexpr (KEEP) g2lds16(base, off[i], lds + ii * 1024);
+          else {
+            int ln = lane;
+            asm volatile("" : "+v"(ln));  // recomputed here, not hoisted out of the caller's loop
+            g2lds16(base, offset(i, tok, w, ln), lds + ii * 1024);
+          }
+        }
       }
     } else {
 #pragma unroll

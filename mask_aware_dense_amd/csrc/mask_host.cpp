@@ -297,7 +297,7 @@ mad_status compile_blocks(mad_plan* p) {
   p->tiling[0].BM = BM0;
   p->tiling[0].BN = BN0;
   p->tiling[1].BM = BM1;
-  p->tiling[1].BN = BN1;
+  p->tiling[1].BN = dkdv_tile_keys(p->k_edges.data(), p->n_kb);
   p->pairs.assign(p->G, 0);
   for (int g = 0; g < p->G; ++g) {
     int64_t n = 0;

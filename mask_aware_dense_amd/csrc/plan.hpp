@@ -4,7 +4,8 @@
 // two kernel tilings of this library:
 //   tiling 0 (forward and dQ kernels): BM0 query rows x BN0 keys, visited as
 //            per-query-tile lists of key tiles (CSR);
-//   tiling 1 (dK/dV kernel):           BM1 query rows x BN1 keys, visited as
+//   tiling 1 (dK/dV kernel):           BM1 query rows x BN1 keys (BN1_FINE
+//            for block-sparse masks of 64-token key blocks), visited as
 //            per-key-tile lists of query tiles (CSC).
 // Every tile is EMPTY (never visited), FULL (no mask arithmetic) or PARTIAL
 // (per-element mask), judged on its in-range elements only.  The O(#tiles)
@@ -33,6 +34,21 @@ namespace mad {
 // these.
 constexpr int BM0 = 128, BN0 = 64;   // forward / dQ
 constexpr int BM1 = 64, BN1 = 128;   // dK / dV
+// dK / dV key tile of block-sparse plans whose key-block edges are all
+// multiples of 64 but not all of 128 (64-token blocks): one key block per
+// tile, so no tile leaves half its waves without keys (a 128-key tile keeps
+// only one of its two blocks in most visited tiles); its workgroup has two
+// waves, and two workgroups share a CU.
+constexpr int BN1_FINE = 64;
+// The dK / dV key-tile width for a block-sparse plan with these key edges.
+inline int dkdv_tile_keys(const int32_t* k_edges, int32_t n_kb) {
+  bool all64 = true, all128 = true;
+  for (int32_t b = 1; b < n_kb; ++b) {  // interior edges (the last one is Tk)
+    all64 &= k_edges[b] % 64 == 0;
+    all128 &= k_edges[b] % 128 == 0;
+  }
+  return (n_kb > 1 && all64 && !all128) ? BN1_FINE : BN1;
+}
 
 enum MaskMode : int32_t { MODE_SLICES = 0, MODE_BLOCKS = 1 };
 enum TileClass : uint8_t { CLS_EMPTY = 0, CLS_FULL = 1, CLS_PARTIAL = 2 };
@@ -62,6 +78,7 @@ struct TilingDev {
   const int32_t* ent_aux;  // SLICES: per entry offset into tile_slices (or -1)
   const int32_t* order;    // [nmajor] longest-first major tile order
   int32_t nmajor, nminor;
+  int32_t BN;              // key-tile width (tiling 1: BN1 or BN1_FINE)
 };
 
 // Device view of the mask source, passed to kernels by value.

@@ -306,7 +306,7 @@ extern "C" mad_status mad_sparse_plan_device(int32_t n_groups, const int32_t* q_
   for (int w = 0; w < 2; ++w) {
     TilingHost& t = p->tiling[w];
     t.BM = w == 0 ? BM0 : BM1;
-    t.BN = w == 0 ? BN0 : BN1;
+    t.BN = w == 0 ? BN0 : dkdv_tile_keys(k_edges, n_kb);
     t.nqt = (p->Tq + t.BM - 1) / t.BM;
     t.nkt = (p->Tk + t.BN - 1) / t.BN;
     geo[w] = TileGeom{t.BM, t.BN, t.nqt, t.nkt, w == 1};
@@ -430,6 +430,7 @@ extern "C" mad_status mad_sparse_plan_device(int32_t n_groups, const int32_t* q_
     d.order = (const int32_t*)(B + f_ord[w]);
     d.nmajor = nmaj[w];
     d.nminor = w == 0 ? p->tiling[0].nkt : p->tiling[1].nqt;
+    d.BN = p->tiling[w].BN;
   }
   MaskDev& m = p->mdev;
   m.mode = MODE_BLOCKS;
