@@ -7,8 +7,8 @@
 //   dV_j  = sum_h sum_i P_ij dO_i,   dK_j = scale sum_h sum_i dS_ij q_i
 //
 // Work decomposition: one workgroup per (KV head, 128-key tile), four waves
-// (per 64-key tile, two waves, for plans of 64-token key blocks)
-// of 32 keys.  K and V of the wave's keys stay in registers as MFMA operands.
+// of 32 keys (per 64-key tile, two waves, for plans of 64-token key blocks).
+// K and V of the wave's keys stay in registers as MFMA operands.
 // The workgroup walks, for each query head of the group, the key tile's list
 // of non-EMPTY 64-row query tiles; the Q / dO tiles and their -LSE/scale and
 // -D rows come in by direct global->LDS loads into a double buffer.
