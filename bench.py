@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--fwd-only", action="store_true", help="time only the forward (profiling aid)")
     ap.add_argument("--suite", action="store_true", help="run every workload family, one JSON line each")
     ap.add_argument("--only", default="", help="with --suite: comma-separated substrings of workload names")
+    ap.add_argument("--runs", type=int, default=1,
+                    help="with --suite: timed runs per single-sequence workload (the line reports the median)")
     ap.add_argument("--doc-seeds", type=int, default=1,
                     help="with --suite: document-length samples per multi-sequence mask (median reported)")
     ap.add_argument("--memory", action="store_true",
@@ -360,6 +362,16 @@ def run_suite(args, torch, mad):
             seeds = {"n": len(vals), "median": float(np.median(vals)), "min": float(min(vals)),
                      "max": float(max(vals)), "first_sample": fwdbwd}
             fwdbwd = seeds["median"]
+        runs = None
+        if args.runs > 1 and not multi_sequence(name):
+            # a single-sequence mask: the same timed steps repeated, the line reports the median
+            vals = [fwdbwd]
+            for _ in range(args.runs - 1):
+                w2, _, _ = r.time(args.steps, args.warmup)
+                vals.append(14.0 * d * pairs * args.steps / w2 / 1e12)
+            runs = {"n": len(vals), "median": float(np.median(vals)), "min": float(min(vals)),
+                    "max": float(max(vals))}
+            fwdbwd = runs["median"]
         rec = {
             "workload": name, "metric": METRIC, "unit": "TFLOP/s", "value": fwdbwd,
             "fwd_tflops": 4.0 * d * pairs / t_fwd / 1e12, "fwdbwd_frac_peak": fwdbwd / PEAK_BF16_TFLOPS,
@@ -373,6 +385,8 @@ def run_suite(args, torch, mad):
         }
         if seeds:
             rec["doc_seeds"] = seeds
+        if runs:
+            rec["runs"] = runs
         print(json.dumps(rec), flush=True)
         del r, plan
         torch.cuda.empty_cache()
