@@ -295,7 +295,7 @@ def suite_workloads(seed):
     for S, Hq, Hkv, b, pct, var in [
         (32768, 64, 8, 128, 20, False), (32768, 64, 8, 128, 50, False), (32768, 64, 8, 128, 80, False),
         (32768, 64, 8, 64, 50, False), (32768, 64, 64, 64, 80, False), (32768, 64, 8, 0, 50, True),
-        (131072, 64, 8, 128, 20, False),
+        (131072, 64, 8, 128, 20, False), (131072, 64, 64, 64, 20, False),
     ]:
         tag = "variable" if var else f"b{b}"
         heads = "MHA 64:64" if Hq == Hkv else f"GQA {Hq}:{Hkv}"
