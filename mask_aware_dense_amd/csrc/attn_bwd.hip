@@ -76,16 +76,28 @@ __global__ __launch_bounds__(256) void delta_kernel(const AttnParams P) {
 // ---------------------------------------------------------------------------
 // Two workgroups per CU at D = 64 / 128; one at D = 256, where the Q / dO
 // operands and the dQ accumulator take 256 registers per lane (421 in all).
-template <int D>
+// HM: the head-major item order (block-sparse masks without a GQA group).
+template <int D, bool HM>
 __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void dq_kernel(const AttnParams P) {
   constexpr int BM = BM0, BN = BN0, NKS = D / 16, NDB = D / 32;
   constexpr int KRS = tile_rs<D, TILE_MIXED>(), KT = tile_elems<D, TILE_MIXED>();
   constexpr int VRS = tile_rs<D, TILE_ROWS>(), VT = tile_elems<D, TILE_ROWS>();
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * (KT + VT)];  // K0 V0 K1 V1
 
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int e = L % P.R, t_ = L / P.R;
-  const int g = t_ % P.Hkv, rank = t_ / P.Hkv;
+  // Work item -> (KV head g, query head e of its group, query tile of rank
+  // `rank` in the longest-first order), arranged so that the workgroups
+  // resident on an XCD share K / V tiles in its L2.  With a GQA group, eight
+  // consecutive items (the group's query heads at one rank) share an XCD
+  // (xcd_remap), so each XCD serves one KV head.  Block-sparse masks without
+  // a group (MHA), whose tiles carry even work, run head by head instead,
+  // ranks in turn over the XCDs: every XCD then works on the same one or two
+  // heads at a time (ranks outermost put eight heads' K / V on each XCD; the
+  // forward fetched 95 GB at 32K, b = 64, s = 0.8).  Masks with uneven tiles
+  // keep ranks outermost, where the longest-first order balances the CUs.
+  constexpr bool mha = HM;  // launched only for P.R == 1
+  const int L = mha ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
+  const int e = mha ? 0 : L % P.R, t_ = mha ? L : L / P.R;
+  const int g = mha ? t_ / P.t.nmajor : t_ % P.Hkv, rank = mha ? t_ % P.t.nmajor : t_ / P.Hkv;
   const int h = g * P.R + e;
   const int qt = sld(P.t.order + rank);
   const int mg = h / P.grp_div;
@@ -280,9 +292,16 @@ hipError_t launch_bwd(const AttnParams& Pq, const AttnParams& Pkv, int D, int nq
     if (err != hipSuccess) return err;
   }
   if ((phases & MAD_BWD_DQ) && nq_items > 0) {
-    if (D == 128) hipLaunchKernelGGL(dq_kernel<128>, dim3(nq_items), dim3(256), 0, stream, Pq);
-    else if (D == 256) hipLaunchKernelGGL(dq_kernel<256>, dim3(nq_items), dim3(256), 0, stream, Pq);
-    else hipLaunchKernelGGL(dq_kernel<64>, dim3(nq_items), dim3(256), 0, stream, Pq);
+    auto run = [&](auto k) { hipLaunchKernelGGL(k, dim3(nq_items), dim3(256), 0, stream, Pq); };
+    if (Pq.R == 1 && Pq.m.mode == MODE_BLOCKS) {
+      if (D == 128) run(dq_kernel<128, true>);
+      else if (D == 256) run(dq_kernel<256, true>);
+      else run(dq_kernel<64, true>);
+    } else {
+      if (D == 128) run(dq_kernel<128, false>);
+      else if (D == 256) run(dq_kernel<256, false>);
+      else run(dq_kernel<64, false>);
+    }
   }
   return hipGetLastError();
 }

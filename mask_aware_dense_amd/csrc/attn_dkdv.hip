@@ -37,7 +37,8 @@ namespace mad {
 // NW waves of 32 keys: a 128-key tile (NW = 4, one workgroup per CU) or,
 // for block-sparse plans of 64-token key blocks, a 64-key tile (NW = 2, two
 // workgroups per CU).
-template <int D, int NW>
+// HM: the head-major item order (block-sparse masks without a GQA group).
+template <int D, int NW, bool HM>
 __global__ __launch_bounds__(64 * NW) void dkdv_kernel(const AttnParams P) {
   constexpr int DO = D == 256 ? 128 : D;  // dK / dV columns per workgroup
   constexpr int BM = BM1, BN = 32 * NW, NKS = D / 16, NDB = DO / 32;
@@ -58,8 +59,17 @@ __global__ __launch_bounds__(64 * NW) void dkdv_kernel(const AttnParams P) {
 
   // Workgroup -> (KV head g, key tile kt of the longest-first order, chunk
   // seg of that column's items).  Consecutive workgroups share g's XCD.
+  // Workgroups go to the XCDs in turn.  Consecutive workgroups take
+  // consecutive KV heads (with 8 KV heads each XCD serves one head and its
+  // group's Q / dO tiles).  Block-sparse masks without a GQA group (MHA),
+  // whose columns carry even work, run head by head instead, so that every
+  // XCD works on the same head's Q / dO tiles at a time rather than on eight
+  // heads'; masks with uneven columns keep the longest-first order across
+  // heads, which balances the CUs.
   const int L = blockIdx.x, S = P.kv_splits;
-  const int g = L % P.Hkv, rest = L / P.Hkv;
+  constexpr bool mha = HM;  // launched only for P.R == 1
+  const int per_head = P.t.nmajor * S;  // workgroups per KV head
+  const int g = mha ? L / per_head : L % P.Hkv, rest = mha ? L % per_head : L / P.Hkv;
   const int kt = sld(P.t.order + rest / S), seg = rest % S;
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, li = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, wave-uniform
@@ -398,14 +408,18 @@ hipError_t launch_dkdv(const AttnParams& P, int D, int n_items, hipStream_t stre
   if (S > 1 && n4 > 0) hipLaunchKernelGGL(zero2_kernel, dim3(nb), dim3(256), 0, stream, P.dk_acc, P.dv_acc, n4);
   const dim3 grid(n_items * S, D == 256 ? 2 : 1);
   auto run = [&](auto k, int nw) { hipLaunchKernelGGL(k, grid, dim3(64 * nw), 0, stream, P); };
+  auto by_d = [&](auto k64, auto k128, auto k256, int nw) {
+    if (D == 128) run(k128, nw);
+    else if (D == 256) run(k256, nw);
+    else run(k64, nw);
+  };
+  const bool hm = P.R == 1 && P.m.mode == MODE_BLOCKS;
   if (P.t.BN == BN1_FINE) {
-    if (D == 128) run(dkdv_kernel<128, 2>, 2);
-    else if (D == 256) run(dkdv_kernel<256, 2>, 2);
-    else run(dkdv_kernel<64, 2>, 2);
+    if (hm) by_d(dkdv_kernel<64, 2, true>, dkdv_kernel<128, 2, true>, dkdv_kernel<256, 2, true>, 2);
+    else by_d(dkdv_kernel<64, 2, false>, dkdv_kernel<128, 2, false>, dkdv_kernel<256, 2, false>, 2);
   } else {
-    if (D == 128) run(dkdv_kernel<128, 4>, 4);
-    else if (D == 256) run(dkdv_kernel<256, 4>, 4);
-    else run(dkdv_kernel<64, 4>, 4);
+    if (hm) by_d(dkdv_kernel<64, 4, true>, dkdv_kernel<128, 4, true>, dkdv_kernel<256, 4, true>, 4);
+    else by_d(dkdv_kernel<64, 4, false>, dkdv_kernel<128, 4, false>, dkdv_kernel<256, 4, false>, 4);
   }
   if (S > 1 && n4 > 0)
     hipLaunchKernelGGL(round2_kernel, dim3(nb), dim3(256), 0, stream, P.dk_acc, P.dv_acc, P.dk, P.dv, n4);

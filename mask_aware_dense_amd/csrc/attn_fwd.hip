@@ -33,7 +33,8 @@ namespace mad {
 #ifndef FWD_PRE_C
 #define FWD_PRE_C 3
 #endif
-template <int D, int NB>
+// HM: the head-major item order (block-sparse masks without a GQA group).
+template <int D, int NB, bool HM>
 __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
   // Score steps of the next key block issued before a block's max is taken
   // (stage B) and P V steps issued before the next block's max (stage C).
@@ -44,9 +45,20 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
   constexpr int VRS = tile_rs<D, TILE_TR>(), VT = tile_elems<D, TILE_TR>();
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * (KT + VT)];  // K0 V0 K1 V1
 
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int e = L % P.R, t_ = L / P.R;
-  const int g = t_ % P.Hkv, rank = t_ / P.Hkv;
+  // Work item -> (KV head g, query head e of its group, query tile of rank
+  // `rank` in the longest-first order), arranged so that the workgroups
+  // resident on an XCD share K / V tiles in its L2.  With a GQA group, eight
+  // consecutive items (the group's query heads at one rank) share an XCD
+  // (xcd_remap), so each XCD serves one KV head.  Block-sparse masks without
+  // a group (MHA), whose tiles carry even work, run head by head instead,
+  // ranks in turn over the XCDs: every XCD then works on the same one or two
+  // heads at a time (ranks outermost put eight heads' K / V on each XCD; the
+  // forward fetched 95 GB at 32K, b = 64, s = 0.8).  Masks with uneven tiles
+  // keep ranks outermost, where the longest-first order balances the CUs.
+  constexpr bool mha = HM;  // launched only for P.R == 1
+  const int L = mha ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
+  const int e = mha ? 0 : L % P.R, t_ = mha ? L : L / P.R;
+  const int g = mha ? t_ / P.t.nmajor : t_ % P.Hkv, rank = mha ? t_ % P.t.nmajor : t_ / P.Hkv;
   const int h = g * P.R + e;
   const int qt = sld(P.t.order + rank);
   const int mg = h / P.grp_div;
@@ -353,9 +365,16 @@ constexpr int FWD_NB = 1;
 
 hipError_t launch_fwd(const AttnParams& P, int D, int n_items, hipStream_t stream) {
   if (n_items <= 0) return hipSuccess;
-  if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, FWD_NB>), dim3(n_items), dim3(256 / FWD_NB), 0, stream, P);
-  else if (D == 256) hipLaunchKernelGGL((fwd_kernel<256, 1>), dim3(n_items), dim3(256), 0, stream, P);
-  else hipLaunchKernelGGL((fwd_kernel<64, FWD_NB>), dim3(n_items), dim3(256 / FWD_NB), 0, stream, P);
+  auto run = [&](auto k, int nb) { hipLaunchKernelGGL(k, dim3(n_items), dim3(256 / nb), 0, stream, P); };
+  if (P.R == 1 && P.m.mode == MODE_BLOCKS) {
+    if (D == 128) run(fwd_kernel<128, FWD_NB, true>, FWD_NB);
+    else if (D == 256) run(fwd_kernel<256, 1, true>, 1);
+    else run(fwd_kernel<64, FWD_NB, true>, FWD_NB);
+  } else {
+    if (D == 128) run(fwd_kernel<128, FWD_NB, false>, FWD_NB);
+    else if (D == 256) run(fwd_kernel<256, 1, false>, 1);
+    else run(fwd_kernel<64, FWD_NB, false>, FWD_NB);
+  }
   return hipGetLastError();
 }
 
