@@ -145,7 +145,7 @@ def _sparse_case(T, b, G, pct, seed, variable):
     return plan, spec
 
 
-@pytest.mark.parametrize("b,variable", [(64, False), (128, False), (100, False), (0, True)])
+@pytest.mark.parametrize("b,variable", [(32, False), (64, False), (128, False), (100, False), (0, True)])
 @pytest.mark.parametrize("pct", [20, 50, 80])
 def test_sparse_plan_bit_exact(b, variable, pct):
     T, G = 2000, 3
