@@ -150,6 +150,21 @@ def test_matches_torch_sdpa_fp64(spec):
         assert np.max(np.abs(g[n] - gref[n])) < 1e-10, n
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("pattern", ["FULL", "CAUSAL", "SLIDING_WINDOW"])
+def test_matches_torch_sdpa_fp64_head_dims(pattern, d):
+    """The head dims the kernels are built for, at the usual scale 1/sqrt(d)."""
+    T, Hq, Hkv = 48, 4, 2
+    spec = [s for s in small_specs(T, seed=7) if s.pattern == pattern][0]
+    scale = 1.0 / math.sqrt(d)
+    q, k, v, do, o_ref, gref, empty = _sdpa_case(spec, T, Hq, Hkv, d, 21 + d, scale)
+    O, L = A.attn_fwd(q, k, v, spec, scale)
+    assert np.max(np.abs((O - o_ref)[~empty.T])) < 1e-10
+    g = A.attn_bwd(q, k, v, do, spec, scale)
+    for n in ("dq", "dk", "dv"):
+        assert np.max(np.abs(g[n] - gref[n])) < 1e-10, n
+
+
 @pytest.mark.parametrize("pattern", ["CAUSAL_DOCUMENT", "SHARED_QUESTION", "GLOBAL_SLIDING", "PREFIX_LM"])
 def test_bwd_finite_differences(pattern):
     T, Hq, Hkv, d, scale = 12, 2, 1, 3, 0.8
