@@ -193,6 +193,7 @@ extern "C" mad_status mad_plan_upload(mad_plan* p, hipStream_t stream) {
     d.nmajor = w == 0 ? t.nqt : t.nkt;
     d.nminor = w == 0 ? t.nkt : t.nqt;
     d.BN = t.BN;
+    d.uniform = t.uniform;
   }
   MaskDev& m = p->mdev;
   m.mode = p->mode;

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void delta_kernel(const AttnParams P) {
 // ---------------------------------------------------------------------------
 // Two workgroups per CU at D = 64 / 128; one at D = 256, where the Q / dO
 // operands and the dQ accumulator take 256 registers per lane (421 in all).
-// HM: the head-major item order (block-sparse masks without a GQA group).
+// HM: the head-major item order (MHA masks whose tiles carry even work).
 template <int D, bool HM>
 __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void dq_kernel(const AttnParams P) {
   constexpr int BM = BM0, BN = BN0, NKS = D / 16, NDB = D / 32;
@@ -88,8 +88,9 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void dq_kernel(const AttnPar
   // `rank` in the longest-first order), arranged so that the workgroups
   // resident on an XCD share K / V tiles in its L2.  With a GQA group, eight
   // consecutive items (the group's query heads at one rank) share an XCD
-  // (xcd_remap), so each XCD serves one KV head.  Block-sparse masks without
-  // a group (MHA), whose tiles carry even work, run head by head instead,
+  // (xcd_remap), so each XCD serves one KV head.  Masks without a group
+  // (MHA) whose tiles carry even work (block-sparse masks, or every list of
+  // one length as under FULL) run head by head instead (the HM variant),
   // ranks in turn over the XCDs: every XCD then works on the same one or two
   // heads at a time (ranks outermost put eight heads' K / V on each XCD; the
   // forward fetched 95 GB at 32K, b = 64, s = 0.8).  Masks with uneven tiles
@@ -293,7 +294,7 @@ hipError_t launch_bwd(const AttnParams& Pq, const AttnParams& Pkv, int D, int nq
   }
   if ((phases & MAD_BWD_DQ) && nq_items > 0) {
     auto run = [&](auto k) { hipLaunchKernelGGL(k, dim3(nq_items), dim3(256), 0, stream, Pq); };
-    if (Pq.R == 1 && Pq.m.mode == MODE_BLOCKS) {
+    if (Pq.R == 1 && (Pq.m.mode == MODE_BLOCKS || Pq.t.uniform)) {
       if (D == 128) run(dq_kernel<128, true>);
       else if (D == 256) run(dq_kernel<256, true>);
       else run(dq_kernel<64, true>);

@@ -37,7 +37,7 @@ namespace mad {
 // NW waves of 32 keys: a 128-key tile (NW = 4, one workgroup per CU) or,
 // for block-sparse plans of 64-token key blocks, a 64-key tile (NW = 2, two
 // workgroups per CU).
-// HM: the head-major item order (block-sparse masks without a GQA group).
+// HM: the head-major item order (MHA masks whose columns carry even work).
 template <int D, int NW, bool HM>
 __global__ __launch_bounds__(64 * NW) void dkdv_kernel(const AttnParams P) {
   constexpr int DO = D == 256 ? 128 : D;  // dK / dV columns per workgroup
@@ -61,8 +61,9 @@ __global__ __launch_bounds__(64 * NW) void dkdv_kernel(const AttnParams P) {
   // seg of that column's items).  Consecutive workgroups share g's XCD.
   // Workgroups go to the XCDs in turn.  Consecutive workgroups take
   // consecutive KV heads (with 8 KV heads each XCD serves one head and its
-  // group's Q / dO tiles).  Block-sparse masks without a GQA group (MHA),
-  // whose columns carry even work, run head by head instead, so that every
+  // group's Q / dO tiles).  Masks without a GQA group (MHA) whose columns
+  // carry even work (block-sparse masks, or every column of one length) run
+  // head by head instead (the HM variant), so that every
   // XCD works on the same head's Q / dO tiles at a time rather than on eight
   // heads'; masks with uneven columns keep the longest-first order across
   // heads, which balances the CUs.
@@ -413,7 +414,7 @@ hipError_t launch_dkdv(const AttnParams& P, int D, int n_items, hipStream_t stre
     else if (D == 256) run(k256, nw);
     else run(k64, nw);
   };
-  const bool hm = P.R == 1 && P.m.mode == MODE_BLOCKS;
+  const bool hm = P.R == 1 && (P.m.mode == MODE_BLOCKS || P.t.uniform);
   if (P.t.BN == BN1_FINE) {
     if (hm) by_d(dkdv_kernel<64, 2, true>, dkdv_kernel<128, 2, true>, dkdv_kernel<256, 2, true>, 2);
     else by_d(dkdv_kernel<64, 2, false>, dkdv_kernel<128, 2, false>, dkdv_kernel<256, 2, false>, 2);

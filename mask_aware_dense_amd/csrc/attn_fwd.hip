@@ -33,7 +33,7 @@ namespace mad {
 #ifndef FWD_PRE_C
 #define FWD_PRE_C 3
 #endif
-// HM: the head-major item order (block-sparse masks without a GQA group).
+// HM: the head-major item order (MHA masks whose tiles carry even work).
 template <int D, int NB, bool HM>
 __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
   // Score steps of the next key block issued before a block's max is taken
@@ -49,8 +49,9 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
   // `rank` in the longest-first order), arranged so that the workgroups
   // resident on an XCD share K / V tiles in its L2.  With a GQA group, eight
   // consecutive items (the group's query heads at one rank) share an XCD
-  // (xcd_remap), so each XCD serves one KV head.  Block-sparse masks without
-  // a group (MHA), whose tiles carry even work, run head by head instead,
+  // (xcd_remap), so each XCD serves one KV head.  Masks without a group
+  // (MHA) whose tiles carry even work (block-sparse masks, or every list of
+  // one length as under FULL) run head by head instead (the HM variant),
   // ranks in turn over the XCDs: every XCD then works on the same one or two
   // heads at a time (ranks outermost put eight heads' K / V on each XCD; the
   // forward fetched 95 GB at 32K, b = 64, s = 0.8).  Masks with uneven tiles
@@ -366,7 +367,7 @@ constexpr int FWD_NB = 1;
 hipError_t launch_fwd(const AttnParams& P, int D, int n_items, hipStream_t stream) {
   if (n_items <= 0) return hipSuccess;
   auto run = [&](auto k, int nb) { hipLaunchKernelGGL(k, dim3(n_items), dim3(256 / nb), 0, stream, P); };
-  if (P.R == 1 && P.m.mode == MODE_BLOCKS) {
+  if (P.R == 1 && (P.m.mode == MODE_BLOCKS || P.t.uniform)) {
     if (D == 128) run(fwd_kernel<128, FWD_NB, true>, FWD_NB);
     else if (D == 256) run(fwd_kernel<256, 1, true>, 1);
     else run(fwd_kernel<64, FWD_NB, true>, FWD_NB);

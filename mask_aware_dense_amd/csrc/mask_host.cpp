@@ -275,6 +275,15 @@ static mad_status build_lists(mad_plan* p, TilingHost& t, bool csc) {
   t.order.resize(nmaj);
   std::iota(t.order.begin(), t.order.end(), 0);
   std::stable_sort(t.order.begin(), t.order.end(), [&](int a, int b) { return work[a] > work[b]; });
+  t.uniform = true;
+  for (int g = 0; g < p->G && t.uniform; ++g)
+    for (int M = 0; M < nmaj; ++M) {
+      const size_t b = (size_t)g * (nmaj + 1);
+      if (t.ptr[b + M + 1] - t.ptr[b + M] != t.ptr[b + 1] - t.ptr[b]) {
+        t.uniform = false;
+        break;
+      }
+    }
   return MAD_OK;
 }
 

@@ -69,6 +69,9 @@ struct TilingHost {
   // longest-first order of the major tiles (work summed over groups)
   std::vector<int32_t> order;
   int64_t n_class[3] = {0, 0, 0};
+  // every major tile's list (in every group) has the same length: the
+  // tiles carry even work, whatever their order
+  bool uniform = false;
 };
 
 // Device view of one tiling, passed to kernels by value.
@@ -79,6 +82,7 @@ struct TilingDev {
   const int32_t* order;    // [nmajor] longest-first major tile order
   int32_t nmajor, nminor;
   int32_t BN;              // key-tile width (tiling 1: BN1 or BN1_FINE)
+  int32_t uniform;         // every list has the same length (even work per tile)
 };
 
 // Device view of the mask source, passed to kernels by value.

@@ -431,6 +431,7 @@ extern "C" mad_status mad_sparse_plan_device(int32_t n_groups, const int32_t* q_
     d.nmajor = nmaj[w];
     d.nminor = w == 0 ? p->tiling[0].nkt : p->tiling[1].nqt;
     d.BN = p->tiling[w].BN;
+    d.uniform = 0;  // block-sparse: the head-major kernels are chosen by the mask mode
   }
   MaskDev& m = p->mdev;
   m.mode = MODE_BLOCKS;
