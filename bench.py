@@ -55,13 +55,14 @@ def parse():
     ap.add_argument("--d", type=int, default=128)
     ap.add_argument("--mask", default="CAUSAL")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-rows", type=int, default=96, help="query rows in the oracle's timed sample")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="query rows in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fwd-only", action="store_true", help="time only the forward (profiling aid)")
     ap.add_argument("--suite", action="store_true", help="run every workload family, one JSON line each")
     ap.add_argument("--only", default="", help="with --suite: comma-separated substrings of workload names")
-    ap.add_argument("--runs", type=int, default=1,
-                    help="with --suite: timed runs per single-sequence workload (the line reports the median)")
+    ap.add_argument("--runs", type=int, default=2,
+                    help="timed runs (warm-up + steps each) of a single-sequence workload; the line reports the "
+                         "median (the pages' protocol: two runs)")
     ap.add_argument("--doc-seeds", type=int, default=1,
                     help="with --suite: document-length samples per multi-sequence mask (median reported)")
     ap.add_argument("--memory", action="store_true",
@@ -93,29 +94,101 @@ def measured_traffic(kernel: str, workload: str):
     return None if k is None else float(k["hbm_bytes_per_launch"])
 
 
+_WORKER = {}
+
+
+def _pool_init(seed, T, Hq, Hkv, d, barrier):
+    """Pool worker start-up (untimed): one BLAS thread (the pool spreads the heads over the cores) and
+    the workload's inputs regenerated from the seed, so tasks carry only a head index.  It never
+    raises (a failing initializer would make the pool start replacement workers without end): a
+    failure is kept and reported by the worker's first task."""
+    try:
+        try:
+            from threadpoolctl import threadpool_limits
+            threadpool_limits(1)
+        except ImportError:
+            pass
+        import torch
+        torch.set_num_threads(1)
+        from mad_inputs import grad_out, qkv
+        _WORKER["qkv"] = qkv(seed, T, T, Hq, Hkv, d)
+        _WORKER["do"] = grad_out(seed, T, Hq, d)
+    except Exception as e:  # noqa: BLE001
+        _WORKER["error"] = repr(e)
+    try:
+        barrier.wait(timeout=600)
+    except Exception:  # noqa: BLE001
+        pass
+
+
+def _cpu_head_task(a):
+    """The oracle, as it stands, on one query head: forward of the sampled rows and their share of the
+    backward."""
+    h, spec, scale, rows = a
+    if "error" in _WORKER:
+        raise RuntimeError(f"oracle worker start-up failed: {_WORKER['error']}")
+    from oracle import attention as A
+    q, k, v = _WORKER["qkv"]
+    R = q.shape[1] // k.shape[1]
+    qh, kh, vh, doh = (A.to_f64(x) for x in (q[:, h:h + 1], k[:, h // R:h // R + 1], v[:, h // R:h // R + 1],
+                                             _WORKER["do"][:, h:h + 1]))
+    t0 = time.perf_counter()
+    A.attn_fwd(qh, kh, vh, spec, scale, rows=rows)
+    A.attn_bwd(qh, kh, vh, doh, spec, scale, rows=rows)
+    return time.perf_counter() - t0
+
+
+def _timed_pool(args, spec, scale, rows, cores):
+    """Wall time of the oracle over every head on `cores` worker processes (start-up excluded)."""
+    import multiprocessing as mp
+    ctx = mp.get_context("spawn")
+    barrier = ctx.Barrier(cores)
+    with ctx.Pool(cores, initializer=_pool_init,
+                  initargs=(args.seed, args.seq, args.hq, args.hkv, args.d, barrier)) as pool:
+        pool.map(time.sleep, [0.05] * cores, chunksize=1)  # returns once the workers have started up
+        t0 = time.perf_counter()
+        pool.map(_cpu_head_task, [(h, spec, scale, rows) for h in range(args.hq)], chunksize=1)
+        return time.perf_counter() - t0
+
+
 def cpu_baseline(args, q, k, v, do, spec, scale):
-    """Oracle (fp64 numpy, as it stands) on a bounded sample of the same workload."""
+    """Oracle (fp64 numpy, as it stands) on a bounded sample of the same workload, heads spread over a
+    process pool on every host core this process may use; plus the tiny reference configuration
+    (T=1024, MHA 4:4, d=64, FULL and CAUSAL) in full."""
     from oracle import attention as A
     from oracle import masks as M
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([x.get("num_threads", 1) for x in threadpool_info() if x.get("user_api") == "blas"] or [1])
-    except Exception:  # noqa: BLE001
-        threads = os.cpu_count() or 1
+    cores = len(os.sched_getaffinity(0))
     rng = np.random.default_rng([args.seed, 9])
     rows = np.sort(rng.choice(args.seq, size=min(args.cpu_rows, args.seq), replace=False))
-    qf, kf, vf, dof = (A.to_f64(x) for x in (q, k, v, do))
-    t0 = time.perf_counter()
-    A.attn_fwd(qf, kf, vf, spec, scale, rows=rows)
-    A.attn_bwd(qf, kf, vf, dof, spec, scale, rows=rows)
-    dt = time.perf_counter() - t0
+    workers = min(cores, args.hq)
+    dt = _timed_pool(args, spec, scale, rows, workers)
     pairs = int(M.allowed(spec, rows, np.arange(args.seq)).sum()) * args.hq
     flop = 14.0 * args.d * pairs
+    # the tiny reference configuration in full (forward, then forward + backward)
+    from mad_inputs import grad_out, qkv
+    tiny = {}
+    for mask in ("FULL", "CAUSAL"):
+        tq, tk, tv = (A.to_f64(x) for x in qkv(0, 1024, 1024, 4, 4, 64))
+        tdo = A.to_f64(grad_out(0, 1024, 4, 64))
+        tspec = M.MaskSpec(mask, 1024, 1024)
+        t0 = time.perf_counter()
+        A.attn_fwd(tq, tk, tv, tspec, 0.125)
+        t_f = time.perf_counter() - t0
+        A.attn_bwd(tq, tk, tv, tdo, tspec, 0.125)
+        t_fb = time.perf_counter() - t0
+        tp = M.pair_count(tspec) * 4
+        tiny[mask] = {"fwd_s": t_f, "fwdbwd_s": t_fb, "fwd_gflops": 4.0 * 64 * tp / t_f / 1e9,
+                      "fwdbwd_gflops": 14.0 * 64 * tp / t_fb / 1e9}
     return {
-        "value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(workers), "kind": "oracle",
         "seconds": dt,
         "sample": f"{len(rows)} seeded query rows x {args.hq} heads of the same workload, fp64 forward + "
-                  f"backward (those rows' share of dQ, dK, dV); effective FLOPs 14*d*pairs",
+                  f"backward (those rows' share of dQ, dK, dV), one head per task on a pool of {workers} "
+                  f"processes (one per core this process may use) with one BLAS thread each; effective "
+                  f"FLOPs 14*d*pairs",
+        "tiny_reference_full": {"config": "T=1024, MHA 4:4, d=64, scale 1/8, seed 0; whole forward and "
+                                          "forward + backward in this process (BLAS at its default threads)",
+                                **tiny},
     }
 
 
@@ -205,7 +278,7 @@ def roofline(kern_ms, pairs, d, T, Hq, workload):
 # ---------------------------------------------------------------------------
 def suite_workloads(seed):
     """(name, builder) pairs; a builder returns (plan, Tq, Tk, Hq, Hkv, d, config dict)."""
-    from mad_inputs import block_scores, doc_lengths, variable_block_sizes
+    from mad_inputs import answer_lengths, block_scores, doc_lengths, variable_block_sizes
     T = 32768
     out = []
 
@@ -213,7 +286,8 @@ def suite_workloads(seed):
         def build(mad):
             sl = mad.mask_slices(pattern, T, **kw)
             return mad.mask_compile(sl, T, T), T, T, 64, 8, 128, {"mask": pattern, "seq_len": T, **{
-                k: (v if not isinstance(v, (list, np.ndarray)) else f"{len(v)} documents") for k, v in kw.items()}}
+                k: (v if not isinstance(v, (list, np.ndarray)) else
+                    (f"{len(v)} documents" if k == "doc_lens" else f"sampled {list(v)}")) for k, v in kw.items()}}
         return build
 
     docs = [int(x) for x in doc_lengths(seed, T)]
@@ -221,7 +295,8 @@ def suite_workloads(seed):
         ("FULL", {}), ("CAUSAL", {}), ("SLIDING_WINDOW", {"window": 4096}),
         ("FULL_DOCUMENT", {"doc_lens": docs}), ("CAUSAL_DOCUMENT", {"doc_lens": docs}),
         ("SLIDING_WINDOW_CAUSAL_DOCUMENT", {"window": 4096, "doc_lens": docs}),
-        ("PREFIX_LM", {}), ("SHARED_QUESTION", {"question": 2048, "n_answers": 4}),
+        ("PREFIX_LM", {}),
+        ("SHARED_QUESTION", {"question": 2048, "answer_lens": [int(x) for x in answer_lengths(seed, T - 2048, 4)]}),
         ("GLOBAL_SLIDING", {"global_len": 256, "window": 2048}), ("CAUSAL_BLOCKWISE", {"block": 2048}),
         ("BLOCK_CAUSAL_DOCUMENT", {"block": 1024, "doc_lens": docs}), ("PREFIX_LM_DOCUMENT", {"doc_lens": docs}),
         ("CAUSAL_BLOCKWISE_LAST", {"block": 2048}),
@@ -317,8 +392,9 @@ def suite_workloads(seed):
 
 
 def multi_sequence(name):
-    """Workloads whose structure depends on a sampled document-length mix."""
-    return "DOCUMENT" in name or "VARLEN" in name
+    """Workloads whose structure depends on sampled lengths (documents, varlen sequences, the answers
+    of a Shared Question mask): the pages time them over 30 independently sampled runs."""
+    return "DOCUMENT" in name or "VARLEN" in name or "SHARED_QUESTION" in name
 
 
 def run_suite(args, torch, mad):
@@ -522,45 +598,75 @@ def ring_share(args, torch, mad, layout, N, C, rank, name, Hq=64, Hkv=8, d=128):
     }
 
 
-def run_memory(args, torch, mad):
-    """Peak device memory of the path (LongCA-bench appendix A.4.2): the forward's and the backward's peak,
-    each the bytes of every live tensor (torch's allocator peak) plus the plan's device block, beside the
-    pages' activation model of standard attention, 11bshd + 5bhs^2 + 2bshd bytes."""
+def activation_model_bytes(b: int, s: int, h: int, d: int) -> int:
+    """The pages' activation-memory model of a standard attention module (LongCA-bench appendix
+    A.4.2): 11bshd + 5bhs^2 + 2bshd, read as bytes for batch b, sequence s, h heads of dim d."""
+    return 11 * b * s * h * d + 5 * b * h * s * s + 2 * b * s * h * d
+
+
+def _alloc_bytes(t) -> int:
+    """Bytes torch's caching allocator counts for a tensor (sizes round up to 512 bytes)."""
+    n = t.numel() * t.element_size()
+    return (n + 511) // 512 * 512
+
+
+def peak_memory_case(torch, mad, mask, T, Hq, Hkv, d, seed, kw=None):
+    """Peak device memory of one forward and one forward+backward (appendix A.4.2): torch's allocator
+    peak over the call's live tensors plus the plan's device block, with the sum those tensors and the
+    plan should come to if the library allocates nothing else, and the free device memory before and
+    after the calls (unchanged if nothing is left allocated)."""
     from mad_inputs import grad_out, qkv
     dev = torch.device("cuda", 0)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    plan = mad.mask_compile(mad.mask_slices(mask, T, **(kw or {})), T, T)
+    plan.upload()
+    pb = plan.device_bytes()
+    q, k, v = (x.to(dev) for x in qkv(seed, T, T, Hq, Hkv, d))
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    scale = 1.0 / np.sqrt(d)
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    mad.attn_fwd(plan, q, k, v, o, lse, scale)
+    torch.cuda.synchronize()
+    free_f = torch.cuda.mem_get_info()[0]
+    fwd_peak = torch.cuda.max_memory_allocated() - base + pb
+    fwd_sum = sum(_alloc_bytes(t) for t in (q, k, v, o, lse)) + pb
+    do = grad_out(seed, T, Hq, d).to(dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(mad.bwd_workspace_bytes(plan, T, T, Hq, Hkv, d), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    free1 = torch.cuda.mem_get_info()[0]
+    mad.attn_bwd(plan, q, k, v, o, do, lse, dq, dk, dv, ws, scale)
+    torch.cuda.synchronize()
+    bwd_peak = torch.cuda.max_memory_allocated() - base + pb
+    bwd_sum = fwd_sum + sum(_alloc_bytes(t) for t in (do, dq, dk, dv, ws))
+    free2 = torch.cuda.mem_get_info()[0]
+    rec = {"fwd_peak_bytes": int(fwd_peak), "fwdbwd_peak_bytes": int(bwd_peak), "plan_device_bytes": int(pb),
+           "fwd_tensors_plus_plan_bytes": int(fwd_sum), "fwdbwd_tensors_plus_plan_bytes": int(bwd_sum),
+           "free_bytes_change_fwd": int(free0) - int(free_f),
+           "free_bytes_change_bwd": int(free1) - int(free2),
+           "standard_attention_activation_model_bytes": activation_model_bytes(1, T, Hq, d)}
+    del q, k, v, o, lse, do, dq, dk, dv, ws, plan
+    return rec
+
+
+def run_memory(args, torch, mad):
+    """Peak device memory of the path (LongCA-bench appendix A.4.2) for GLOBAL_SLIDING MHA (the pages'
+    plotted case) and CAUSAL GQA from 1K to 48K, beside the pages' activation model of standard
+    attention."""
     for mask, Hq, Hkv in [("GLOBAL_SLIDING", 64, 64), ("CAUSAL", 64, 8)]:
         for T in [1024, 2048, 4096, 8192, 16384, 32768, 49152]:
             d = 128
-            torch.cuda.synchronize()
-            torch.cuda.empty_cache()
-            base = torch.cuda.memory_allocated()
-            torch.cuda.reset_peak_memory_stats()
             kw = {"global_len": 256, "window": 2048} if mask == "GLOBAL_SLIDING" else {}
-            plan = mad.mask_compile(mad.mask_slices(mask, T, **kw), T, T)
-            plan.upload()
-            pb = plan.device_bytes()
-            q, k, v = (x.to(dev) for x in qkv(args.seed, T, T, Hq, Hkv, d))
-            o = torch.empty_like(q)
-            lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
-            scale = 1.0 / np.sqrt(d)
-            mad.attn_fwd(plan, q, k, v, o, lse, scale)
-            torch.cuda.synchronize()
-            fwd_peak = torch.cuda.max_memory_allocated() - base + pb
-            do = grad_out(args.seed, T, Hq, d).to(dev)
-            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-            ws = torch.empty(mad.bwd_workspace_bytes(plan, T, T, Hq, Hkv, d), dtype=torch.uint8, device=dev)
-            mad.attn_bwd(plan, q, k, v, o, do, lse, dq, dk, dv, ws, scale)
-            torch.cuda.synchronize()
-            bwd_peak = torch.cuda.max_memory_allocated() - base + pb
-            b, sd, hd = 1, T, Hq * d
-            model = 11 * b * sd * hd + 5 * b * Hq * sd * sd + 2 * b * sd * hd
+            rec = peak_memory_case(torch, mad, mask, T, Hq, Hkv, d, args.seed, kw)
             rec = {"workload": f"peak memory {mask} {'MHA' if Hq == Hkv else 'GQA'} {Hq}:{Hkv} T={T} d={d}",
-                   "seq_len": T, "mask": mask, "heads_q": Hq, "heads_kv": Hkv, "head_dim": d,
-                   "fwd_peak_bytes": int(fwd_peak), "fwdbwd_peak_bytes": int(bwd_peak), "plan_device_bytes": int(pb),
-                   "standard_attention_activation_model_bytes": int(model),
+                   "seq_len": T, "mask": mask, "heads_q": Hq, "heads_kv": Hkv, "head_dim": d, **rec,
                    "note": "peaks count every live tensor of the call (inputs, outputs, workspace) plus the plan"}
             print(json.dumps(rec), flush=True)
-            del q, k, v, o, lse, do, dq, dk, dv, ws, plan
 
 
 def mfma_sustained(torch, mad, n_wg=2048, iters=2048):
@@ -620,10 +726,17 @@ def main():
     flop_bwd = 10.0 * d * pairs
 
     r = Runner(torch, mad, plan, T, T, Hq, Hkv, d, args.seed)
-    wall, kern_ms, kern_med = r.time(args.steps, args.warmup, args.fwd_only)
+    # the pages' protocol for a single-sequence mask: two runs of warm-up + timed steps, the median
+    # reported (appendix A.4); each run times exactly `steps` steps between synchronisations
+    runs = [r.time(args.steps, args.warmup, args.fwd_only) for _ in range(max(1, args.runs))]
+    walls = [x[0] for x in runs]
+    wall = float(np.median(walls))
+    kern_ms = {n: float(np.mean([x[1][n] for x in runs])) for n in runs[0][1]}
+    kern_med = {n: float(np.median([x[2][n] for x in runs])) for n in runs[0][2]}
     ms_step = wall * 1e3 / args.steps
     fwd_tflops = flop_fwd / (kern_ms["fwd"] * 1e-3) / 1e12
-    value = fwd_tflops if args.fwd_only else (flop_fwd + flop_bwd) * args.steps / wall / 1e12
+    run_vals = [(flop_fwd if args.fwd_only else flop_fwd + flop_bwd) * args.steps / w / 1e12 for w in walls]
+    value = fwd_tflops if args.fwd_only else float(np.median(run_vals))
     workload = (f"{args.mask} attention {'fwd' if args.fwd_only else 'fwd+bwd'}, packed batch 1, "
                 f"T={T}, GQA {Hq}:{Hkv}, head_dim {d}")
 
@@ -647,6 +760,8 @@ def main():
         "fwdbwd_frac_peak": value / PEAK_BF16_TFLOPS,
         "kernel_ms_mean": kern_ms,
         "kernel_ms_median": kern_med,
+        "runs": {"n": len(runs), "values": run_vals, "ms_per_step": [w * 1e3 / args.steps for w in walls],
+                 "reported": "median"},
         "unmasked_pairs": pairs,
         "mask_compile_s": compile_s,
         "roofline": roofline(kern_ms, pairs, d, T, Hq, workload),

@@ -108,7 +108,10 @@ typedef struct {
   int32_t n_answers;       /* SHARED_QUESTION: answers split the rest equally, the last takes the remainder */
   int32_t global_len;      /* GLOBAL_SLIDING: G */
   int32_t block;           /* CAUSAL_BLOCKWISE*, BLOCK_CAUSAL_DOCUMENT* block size (> 0) */
-  const int32_t* doc_lens; /* *_DOCUMENT: host array of n_docs lengths summing to T */
+  const int32_t* doc_lens; /* *_DOCUMENT: host array of n_docs lengths summing to T;
+                              SHARED_QUESTION: optional n_docs answer lengths summing to
+                              T - question, used instead of the equal split (the sampled
+                              answer lengths of LongCA-bench appendix A.4) */
   int32_t n_docs;
 } mad_mask_params;
 
@@ -166,18 +169,36 @@ mad_status mad_block_topk(const float* scores, int32_t n_groups, int32_t n_qb, i
  * ------------------------------------------------------------------------- */
 typedef struct mad_plan mad_plan;
 
-/* Compile n slices for a Tq x Tk mask.  Every slice must satisfy
- * 0 <= q0 <= q1 <= Tq, 0 <= k0 <= k1 <= Tk, a known type and window >= 0.
- * Host only: call mad_plan_upload before attention calls.  The plan is owned
- * by the caller and released with mad_plan_destroy. */
+/* Compile n slices for a Tq x Tk mask (LongCA-bench section 2.1 "Data
+ * preparation": one interface for every mask pattern and for packed
+ * variable-length sequences; section 2.2 "Attention kernel": each kernel's
+ * inputs come from one unified representation; appendix A.3, FlexAttention:
+ * a block mask that compiles into a dense O(S^2) array costs most of the
+ * memory, so this plan is O(tiles + slices)).
+ *   slices: host array of n mad_slice (n = 0 gives an all-EMPTY mask); each
+ *     must satisfy 0 <= q0 <= q1 <= Tq, 0 <= k0 <= k1 <= Tk, a known type,
+ *     window >= 0, and window == 0 on FULL slices.
+ *   out: receives a plan owned by the caller (release with mad_plan_destroy).
+ * Host only: call mad_plan_upload before attention calls.  Errors:
+ * MAD_ERR_INVALID for a bad slice or size (nothing is allocated),
+ * MAD_ERR_NOMEM if host memory runs out. */
 mad_status mad_mask_compile(const mad_slice* slices, int64_t n, int32_t Tq, int32_t Tk,
                             mad_plan** out);
 
-/* Compile a block-sparse mask.  q_edges (n_qb + 1 entries) and k_edges
- * (n_kb + 1) are strictly increasing block boundaries from 0 to Tq and Tk;
- * keep is the bitmap of mad_block_topk for n_groups mask groups.  Query head
- * h uses mask group h / (Hq / n_groups), so n_groups = Hkv shares one keep set
- * per GQA group and n_groups = Hq (MHA) gives one per head.  Host only. */
+/* Compile a block-sparse mask (LongCA-bench appendix A.2 "Block-sparse
+ * mask generation": the attention map cut into a grid of query and key
+ * blocks, uniform or of variable sizes, a top-k key-block set per query
+ * block, one set per head under MHA and per KV-head group under GQA;
+ * appendix A.3 and A.5.2: FlashInfer's per-element metadata and
+ * FlexAttention's O(S^2) block mask run out of memory at long sequences and
+ * small blocks, so the plan holds the bitmap and per-tile lists only).
+ *   q_edges (n_qb + 1 entries), k_edges (n_kb + 1): host int32, strictly
+ *     increasing block boundaries from 0 to Tq and Tk.
+ *   keep: host uint64 bitmap of mad_block_topk, [n_groups][n_qb][ceil(n_kb/64)].
+ * Query head h uses mask group h / (Hq / n_groups), so n_groups = Hkv shares
+ * one keep set per GQA group and n_groups = Hq (MHA) gives one per head.
+ * Host only; the plan is owned by the caller.  Errors: MAD_ERR_INVALID for
+ * bad edges or sizes, MAD_ERR_NOMEM if host memory runs out. */
 mad_status mad_sparse_plan(int32_t n_groups, const int32_t* q_edges, int32_t n_qb,
                            const int32_t* k_edges, int32_t n_kb, const uint64_t* keep,
                            mad_plan** out);
@@ -223,10 +244,16 @@ mad_status mad_plan_lists(const mad_plan* plan, int32_t which, int64_t* n_ptr, i
  * owned by the plan; synchronises `stream`).  Idempotent. */
 mad_status mad_plan_upload(mad_plan* plan, hipStream_t stream);
 
-/* Plan statistics.  pairs_per_group (n_groups entries, may be NULL) receives
- * the exact number of allowed (i, j) pairs of each mask group;
- * n_full/n_partial/n_empty (may be NULL) receive the tile-class counts of
- * tiling `which` (0 = forward/dQ tiling, 1 = dK/dV tiling) summed over groups. */
+/* Plan statistics (LongCA-bench appendix A.4: throughput is reported in
+ * FLOPS; the effective count takes only the unmasked (query, key) pairs, so
+ * it needs the exact pair count of the mask).
+ *   pairs_per_group: host int64 [n_groups] (may be NULL), the exact number of
+ *     allowed (i, j) pairs of each mask group;
+ *   n_full / n_partial / n_empty: host int64 (each may be NULL), the tile-class
+ *     counts of tiling `which` (0 = forward/dQ tiling, 1 = dK/dV tiling) summed
+ *     over groups.
+ * Reads host metadata only (a GPU-compiled plan keeps its counts on the host).
+ * Errors: MAD_ERR_INVALID for a NULL plan or a tiling other than 0 / 1. */
 mad_status mad_plan_stats(const mad_plan* plan, int32_t which, int64_t* pairs_per_group,
                           int64_t* n_full, int64_t* n_partial, int64_t* n_empty);
 
@@ -245,11 +272,18 @@ mad_status mad_plan_info(const mad_plan* plan, int32_t which, int32_t* Tq, int32
                          int32_t* n_groups, int32_t* BM, int32_t* BN, int32_t* n_qt,
                          int32_t* n_kt);
 
-/* Export tiling `which` for mask group `group` to host arrays:
- * classes [n_qt * n_kt] (0 EMPTY, 1 FULL, 2 PARTIAL, row-major by query tile),
- * csr_ptr [n_qt + 1] / csr_idx [entries] (ascending key tiles per query tile),
- * csc_ptr [n_kt + 1] / csc_idx [entries] (ascending query tiles per key tile).
- * Any output may be NULL; list lengths equal the number of non-EMPTY tiles. */
+/* Export tiling `which` for mask group `group` to host arrays, for
+ * inspection and tests (LongCA-bench section 2.2: one representation the
+ * kernel inputs come from; section 3.1: a column-wise mask representation
+ * such as FlashMask's cannot express every pattern, which per-tile classes
+ * and visit lists do):
+ *   classes [n_qt * n_kt] (0 EMPTY, 1 FULL, 2 PARTIAL, row-major by query tile),
+ *   csr_ptr [n_qt + 1] / csr_idx [entries] (ascending key tiles per query tile),
+ *   csc_ptr [n_kt + 1] / csc_idx [entries] (ascending query tiles per key tile).
+ * Any output may be NULL; list lengths equal the number of non-EMPTY tiles
+ * (size the arrays with mad_plan_info and a first call for the ptr arrays).
+ * Errors: MAD_ERR_INVALID for a NULL plan, a bad tiling or group; a
+ * GPU-compiled plan is copied back synchronously (MAD_ERR_HIP on failure). */
 mad_status mad_plan_export(const mad_plan* plan, int32_t which, int32_t group, uint8_t* classes,
                            int64_t* csr_ptr, int32_t* csr_idx, int64_t* csc_ptr, int32_t* csc_idx);
 
@@ -271,23 +305,53 @@ mad_status mad_attn_fwd(const mad_plan* plan, const void* q, const void* k, cons
                         void* o, float* lse, int32_t Tq, int32_t Tk, int32_t Hq, int32_t Hkv,
                         int32_t d, const int64_t* strides, float scale, hipStream_t stream);
 
-/* Bytes of device workspace mad_attn_bwd needs: two fp32 [Hq][Tq rounded up
+/* Bytes of device workspace mad_attn_bwd needs (LongCA-bench section 3.2:
+ * the backward is the harder pass and only some kernels have one; appendix
+ * A.4.2: peak memory is a metric of its own, and this workspace is all the
+ * backward uses beyond its inputs and outputs): two fp32 [Hq][Tq rounded up
  * to 128] arrays holding -D (D = rowsum(dO * O)) and -LSE / scale per row
  * (-inf for rows with no allowed key and for padding rows), and, when the
  * plan's key-tile columns are uneven enough that the dK/dV kernel cuts the
- * longest ones between several workgroups, two fp32 [Tk][Hkv][d] sums for
- * dK and dV.  Depends on the plan, so query it per plan. */
+ * longest ones between several workgroups (mad_bwd_kv_splits > 1), two fp32
+ * [Tk][Hkv][d] sums for dK and dV.  Depends on the plan and on the compute
+ * units of the current device, so query it per plan.  Host only; launches
+ * nothing.  Errors: MAD_ERR_INVALID for NULL arguments or bad sizes,
+ * MAD_ERR_UNSUPPORTED for a head dim other than 64 / 128 / 256. */
 mad_status mad_bwd_workspace_bytes(const mad_plan* plan, int32_t Tq, int32_t Tk, int32_t Hq,
                                    int32_t Hkv, int32_t d, size_t* bytes);
 
-/* Backward of the forward above for upstream gradient d_o, given o and lse
- * (normally the forward's; for a ring step the merged global ones, so the
- * step's share of the global gradient is produced).  Runs the delta pre-pass
- * D = rowsum(d_o * o) (and LSE / scale) into the workspace, then the dK/dV
- * kernel and the dQ kernel.  dq, dk, dv are overwritten.  workspace must be 256-byte aligned
- * and at least mad_bwd_workspace_bytes long; q/k/v/o/d_o are not modified.
- * Results are bit-reproducible, except dk/dv of plans whose columns are cut
- * (their fp32 partial sums are added in arrival order). */
+/* Workgroups per key-tile column that the backward's dK/dV kernel uses for
+ * this plan and head layout (LongCA-bench section 3.2, the backward).  1: each
+ * key tile's dK / dV is accumulated by one workgroup and stored as bf16
+ * directly (bit-reproducible).  S > 1 (at most 8): the columns are cut into S
+ * chunks whose fp32 partial sums are added atomically into the workspace and
+ * rounded by a second kernel; chosen when the longest column holds more than
+ * half of one compute unit's average share of the items, read against the
+ * current device's compute-unit count (256 on MI355X, also the value used
+ * when no device is visible).  Host only; launches nothing.
+ *   splits: receives S.
+ * Errors: MAD_ERR_INVALID for NULL arguments, Hq % Hkv != 0 or mask groups
+ * that do not divide Hq. */
+mad_status mad_bwd_kv_splits(const mad_plan* plan, int32_t Hq, int32_t Hkv, int32_t* splits);
+
+/* Backward of the forward above (LongCA-bench section 3.2: the backward pass
+ * is the common bottleneck and several sparse kernels have none; section
+ * 2.3: a ring step's backward takes the merged O and LSE) for upstream
+ * gradient d_o, given o and lse (normally the forward's; for a ring step the
+ * merged global ones, so the step's share of the global gradient is
+ * produced).  Runs the delta pre-pass D = rowsum(d_o * o) (and LSE / scale)
+ * into the workspace, then the dK/dV kernel and the dQ kernel.
+ *   q, k, v: as for mad_attn_fwd (strided views allowed).
+ *   o, d_o, dq: device bf16 [Tq, Hq, d] packed; dk, dv: device bf16
+ *     [Tk, Hkv, d] packed; lse: device fp32 [Hq, Tq].  All 16-byte aligned
+ *     (lse 4-byte).  dq, dk, dv are overwritten; dK / dV rows of keys no
+ *     query sees are set to 0.
+ *   workspace: device, 256-byte aligned, at least mad_bwd_workspace_bytes
+ *     long, owned by the caller; its contents on entry do not matter.
+ * q/k/v/o/d_o/lse are not modified.  Results are bit-reproducible, except
+ * dk/dv of plans whose columns are cut (mad_bwd_kv_splits > 1: their fp32
+ * partial sums are added in arrival order).  Errors as for mad_attn_fwd, plus
+ * MAD_ERR_INVALID for a missing or undersized workspace. */
 mad_status mad_attn_bwd(const mad_plan* plan, const void* q, const void* k, const void* v,
                         const void* o, const void* d_o, const float* lse, void* dq, void* dk,
                         void* dv, void* workspace, size_t workspace_bytes, int32_t Tq,

@@ -18,6 +18,7 @@ import numpy as np
 
 __all__ = [
     "qkv", "grad_out", "qkv_device", "grad_out_device", "doc_lengths", "block_scores", "variable_block_sizes",
+    "answer_lengths",
 ]
 
 
@@ -105,3 +106,12 @@ def variable_block_sizes(seed: int, T: int, lo: int = 32, hi: int = 256) -> np.n
         out.append(b)
         total += b
     return np.asarray(out, dtype=np.int64)
+
+
+def answer_lengths(seed: int, rest: int, n_answers: int) -> np.ndarray:
+    """Answer lengths of a Shared Question mask (int64, n_answers entries summing to `rest`):
+    n_answers - 1 cut points drawn uniformly from 0..rest and sorted."""
+    rng = np.random.default_rng([int(seed), 4])
+    cuts = np.sort(rng.integers(0, rest + 1, size=max(n_answers - 1, 0)))
+    edges = np.concatenate([[0], cuts, [rest]]).astype(np.int64)
+    return np.diff(edges)

@@ -16,7 +16,7 @@ import numpy as np
 
 __all__ = [
     "MadError", "lib", "Plan", "mask_slices", "ring_step_slices", "varlen_slices", "block_topk", "sparse_plan_device",
-    "mask_compile", "sparse_plan", "attn_fwd", "attn_bwd", "attn_bwd_phases", "bwd_workspace_bytes",
+    "mask_compile", "sparse_plan", "attn_fwd", "attn_bwd", "attn_bwd_phases", "bwd_workspace_bytes", "bwd_kv_splits",
     "block_mask", "block_mask_workspace_bytes", "lse_merge", "Ring", "BWD_DELTA", "BWD_DKDV", "BWD_DQ", "BWD_ALL",
     "PATTERNS", "SLICE_DTYPE",
 ]
@@ -76,6 +76,7 @@ _SIGS = {
     "mad_plan_device_bytes": (_I32, [_VP, ctypes.POINTER(ctypes.c_size_t)]),
     "mad_attn_fwd": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP, _F32, _VP]),
     "mad_bwd_workspace_bytes": (_I32, [_VP, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)]),
+    "mad_bwd_kv_splits": (_I32, [_VP, _I32, _I32, _PI32]),
     "mad_attn_bwd": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
                             _I32, _I32, _I32, _I32, _I32, _VP, _F32, _VP]),
     "mad_attn_bwd_phases": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
@@ -138,9 +139,17 @@ def _stream(stream):
 # --------------------------------------------------------------------------- masks
 
 def mask_slices(pattern, T: int, window: int = 4096, prefix: int = -1, question: int = 2048,
-                n_answers: int = 4, global_len: int = 256, block: int = 1024, doc_lens=None) -> np.ndarray:
-    """Slices (structured array of SLICE_DTYPE) of a static pattern over a T x T mask."""
+                n_answers: int = 4, global_len: int = 256, block: int = 1024, doc_lens=None,
+                answer_lens=None) -> np.ndarray:
+    """Slices (structured array of SLICE_DTYPE) of a static pattern over a T x T mask.
+
+    answer_lens (SHARED_QUESTION only) gives the answers' lengths instead of the equal split; the
+    C ABI takes them in the doc_lens field."""
     pid = PATTERNS[pattern] if isinstance(pattern, str) else int(pattern)
+    if answer_lens is not None:
+        if doc_lens is not None:
+            raise ValueError("give doc_lens or answer_lens, not both")
+        doc_lens = answer_lens
     docs = np.ascontiguousarray(np.asarray([] if doc_lens is None else doc_lens, dtype=np.int32))
     prm = _Params(window, prefix, question, n_answers, global_len, block,
                   docs.ctypes.data_as(_PI32) if docs.size else None, docs.size)
@@ -286,10 +295,63 @@ def _qkv_strides(q, k, v):
     return arr
 
 
+def _check_tensors(q, k, v, packed, lse):
+    """Argument checks the C ABI cannot make from raw pointers: dtypes, exact shapes, one device, and
+    packed (contiguous) layouts for every tensor the kernels address as packed.  q / k / v may be
+    strided views (their strides are passed on); `packed` maps names to (tensor, shape) pairs."""
+    import torch
+    if len(q.shape) != 3 or len(k.shape) != 3 or len(v.shape) != 3:
+        raise MadError(1, "q, k, v must be 3-D [tokens, heads, head_dim]")
+    if tuple(v.shape) != tuple(k.shape):
+        raise MadError(1, f"v shape {tuple(v.shape)} differs from k shape {tuple(k.shape)}")
+    if q.shape[2] != k.shape[2]:
+        raise MadError(1, "q and k head dims differ")
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16:
+            raise MadError(1, f"{name} must be bfloat16, got {t.dtype}")
+        if t.device != dev:
+            raise MadError(1, f"{name} is on {t.device}, q on {dev}")
+    for name, (t, shape) in packed.items():
+        if t is None:
+            raise MadError(1, f"{name} must not be None")
+        if tuple(t.shape) != tuple(shape):
+            raise MadError(1, f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+        if t.dtype != torch.bfloat16:
+            raise MadError(1, f"{name} must be bfloat16, got {t.dtype}")
+        if t.device != dev:
+            raise MadError(1, f"{name} is on {t.device}, q on {dev}")
+        if not t.is_contiguous():
+            raise MadError(1, f"{name} must be contiguous (packed [tokens, heads, head_dim])")
+    if lse is not None:
+        Hq, Tq = q.shape[1], q.shape[0]
+        if tuple(lse.shape) != (Hq, Tq):
+            raise MadError(1, f"lse must have shape {(Hq, Tq)}, got {tuple(lse.shape)}")
+        if lse.dtype != torch.float32:
+            raise MadError(1, f"lse must be float32, got {lse.dtype}")
+        if lse.device != dev:
+            raise MadError(1, f"lse is on {lse.device}, q on {dev}")
+        if not lse.is_contiguous():
+            raise MadError(1, "lse must be contiguous [heads, tokens]")
+    if dev.type != "cuda":
+        raise MadError(1, f"tensors must be on a GPU, got {dev}")
+    if dev.index is not None and torch.cuda.is_available() and dev.index != torch.cuda.current_device():
+        raise MadError(1, f"tensors are on {dev} but the current device is cuda:{torch.cuda.current_device()}")
+
+
+def _check_workspace(workspace):
+    if workspace is None:
+        return 0
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise MadError(1, "workspace must be a contiguous GPU tensor")
+    return workspace.numel() * workspace.element_size()
+
+
 def attn_fwd(plan: Plan, q, k, v, o, lse, scale: float, stream=None):
     """Forward into preallocated o [Tq,Hq,d] bf16 and lse [Hq,Tq] fp32 (torch CUDA tensors)."""
     Tq, Hq, d = q.shape
     Tk, Hkv, _ = k.shape
+    _check_tensors(q, k, v, {"o": (o, (Tq, Hq, d))}, lse)
     st = _qkv_strides(q, k, v)
     _check(lib().mad_attn_fwd(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), Tq, Tk, Hq, Hkv, d,
                               st, float(scale), _stream(stream)))
@@ -301,12 +363,21 @@ def bwd_workspace_bytes(plan: Plan, Tq: int, Tk: int, Hq: int, Hkv: int, d: int)
     return n.value
 
 
+def bwd_kv_splits(plan: Plan, Hq: int, Hkv: int) -> int:
+    """Workgroups per key-tile column of the backward's dK/dV kernel (1: no cut columns)."""
+    n = ctypes.c_int32()
+    _check(lib().mad_bwd_kv_splits(plan.handle, Hq, Hkv, ctypes.byref(n)))
+    return n.value
+
+
 def attn_bwd(plan: Plan, q, k, v, o, d_o, lse, dq, dk, dv, workspace, scale: float, stream=None):
     """Backward into preallocated dq, dk, dv; workspace is a device buffer (uint8 tensor)."""
     Tq, Hq, d = q.shape
     Tk, Hkv, _ = k.shape
+    _check_tensors(q, k, v, {"o": (o, (Tq, Hq, d)), "d_o": (d_o, (Tq, Hq, d)), "dq": (dq, (Tq, Hq, d)),
+                             "dk": (dk, (Tk, Hkv, d)), "dv": (dv, (Tk, Hkv, d))}, lse)
     st = _qkv_strides(q, k, v)
-    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    nbytes = _check_workspace(workspace)
     _check(lib().mad_attn_bwd(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
                               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes, Tq, Tk, Hq, Hkv, d,
                               st, float(scale), _stream(stream)))
@@ -317,8 +388,10 @@ def attn_bwd_phases(plan: Plan, q, k, v, o, d_o, lse, dq, dk, dv, workspace, sca
     """One or more of the backward's launches (BWD_DELTA, BWD_DKDV, BWD_DQ bit set)."""
     Tq, Hq, d = q.shape
     Tk, Hkv, _ = k.shape
+    _check_tensors(q, k, v, {"o": (o, (Tq, Hq, d)), "d_o": (d_o, (Tq, Hq, d)), "dq": (dq, (Tq, Hq, d)),
+                             "dk": (dk, (Tk, Hkv, d)), "dv": (dv, (Tk, Hkv, d))}, lse)
     st = _qkv_strides(q, k, v)
-    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    nbytes = _check_workspace(workspace)
     _check(lib().mad_attn_bwd_phases(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
                                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes, Tq, Tk, Hq, Hkv, d,
                                      st, float(scale), int(phases), _stream(stream)))

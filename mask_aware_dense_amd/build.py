@@ -35,8 +35,9 @@ def flags():
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", os.path.join(ROOT, "include"), "-Wno-unused-result",
         # MFMA results in arch VGPRs: the score tiles feed VALU softmax code
-        # directly, and the register allocator then keeps every kernel
-        # spill-free (measured: forward 58.9 -> 22.7 ms at 32K causal)
+        # directly, and the register allocator then keeps the kernels
+        # spill-free but for the one listed in VALIDATED_SCRATCH (measured:
+        # forward 58.9 -> 22.7 ms at 32K causal)
         "-mllvm", "-amdgpu-mfma-vgpr-form",
         # the D = 256 step loops are longer than the default full-unroll
         # budget; partly unrolled, their operand arrays would be indexed at
@@ -45,12 +46,50 @@ def flags():
     ]
 
 
+# Scratch (private memory) bytes per lane of every kernel, as validated by the
+# GPU parity tests.  A kernel that spills registers adds scratch loads and
+# stores to the vector-memory counter that the direct global->LDS copies are
+# waited on with, so a changed register allocation must not slip in
+# unnoticed: the build fails when any kernel's scratch size differs from its
+# recorded value (0 for every kernel not listed).
+VALIDATED_SCRATCH = {
+    # head dim 256, 64-key tiles in two-wave workgroups: 7 registers spilled
+    "_ZN3mad11dkdv_kernelILi256ELi2ELb0EEEvNS_10AttnParamsE": 24,
+    "_ZN3mad11dkdv_kernelILi256ELi2ELb1EEEvNS_10AttnParamsE": 24,
+}
+
+
+def _scratch_sizes(stderr: str) -> dict:
+    """Kernel name -> ScratchSize [bytes/lane] from -Rpass-analysis=kernel-resource-usage remarks."""
+    out, cur = {}, None
+    for line in stderr.splitlines():
+        if "remark:" not in line:
+            continue
+        text = line.split("remark:", 1)[1].strip()
+        if text.startswith("Function Name:"):
+            cur = text.split(":", 1)[1].split()[0]
+        elif text.startswith("ScratchSize") and cur is not None:
+            out[cur] = int(text.split(":", 1)[1].split()[0])
+    return out
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [hipcc(), *flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    hip = src.endswith(".hip")
+    cmd = [hipcc(), *flags(), *(["-Rpass-analysis=kernel-resource-usage"] if hip else []), "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if hip:
+        sizes = _scratch_sizes(r.stderr)
+        with open(os.path.join(CSRC, src)) as f:
+            if "__global__" in f.read() and not sizes:
+                raise RuntimeError(f"{src}: no kernel resource-usage remarks in the compiler output")
+        bad = {k: v for k, v in sizes.items() if v != VALIDATED_SCRATCH.get(k, 0)}
+        if bad:
+            raise RuntimeError(f"{src}: kernel scratch sizes differ from the validated ones "
+                               f"(bytes/lane): {bad}; expected {VALIDATED_SCRATCH} (others 0)")
     return obj
 
 

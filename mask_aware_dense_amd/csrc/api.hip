@@ -4,6 +4,7 @@
 // anything, returns a mad_status, and records a message for mad_last_error()
 // on the calling thread.  Kernels run on the caller's stream.
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <string>
 
@@ -65,12 +66,32 @@ mad_status check_common(const char* fn, const mad_plan* p, const void* q, const 
   return MAD_OK;
 }
 
+// Compute units of the current device (cached per device); 256, the MI355X
+// count, when no device is visible (host-only use of the queries).
+int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (!n) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 // Workgroups per key-tile column of the dK/dV kernel.  The kernel runs one
-// workgroup per CU (256 CUs); when its longest column holds more than half of
-// one CU's average share of the items, that column alone would set the
-// kernel's length, so every column is cut into S chunks with the longest
-// chunk at most that half-share (S capped at 8).  Balanced masks keep S = 1
-// (CAUSAL 32K GQA: the longest column is a quarter of the average share).
+// workgroup per CU; when its longest column holds more than half of one CU's
+// average share of the items, that column alone would set the kernel's
+// length, so every column is cut into S chunks with the longest chunk at
+// most that half-share (S capped at 8).  Balanced masks keep S = 1 (CAUSAL
+// 32K GQA: the longest column is a quarter of the average share).
 int dkdv_splits(const mad_plan* p, int32_t Hq, int32_t Hkv) {
   const TilingHost& t = p->tiling[1];
   const int R = Hq / Hkv, grp_div = Hq / p->G, nk = t.nkt;
@@ -87,8 +108,8 @@ int dkdv_splits(const mad_plan* p, int32_t Hq, int32_t Hkv) {
       mx = std::max(mx, n);
     }
   if (total == 0) return 1;
-  constexpr int64_t kCUs = 256;
-  return (int)std::min<int64_t>(8, std::max<int64_t>(1, (mx * 2 * kCUs + total - 1) / total));
+  const int64_t cus = device_cus();
+  return (int)std::min<int64_t>(8, std::max<int64_t>(1, (mx * 2 * cus + total - 1) / total));
 }
 
 AttnParams base_params(const mad_plan* p, int which, const void* q, const void* k, const void* v, int32_t Tq,
@@ -269,6 +290,15 @@ extern "C" mad_status mad_bwd_workspace_bytes(const mad_plan* p, int32_t Tq, int
   const size_t tq_pad = ((size_t)Tq + 127) / 128 * 128;
   *bytes = (2 * (size_t)Hq * tq_pad * 4 + 255) / 256 * 256;
   if (Hq % Hkv == 0 && Hq % p->G == 0 && dkdv_splits(p, Hq, Hkv) > 1) *bytes += 2 * (size_t)Tk * Hkv * d * 4;
+  return MAD_OK;
+}
+
+extern "C" mad_status mad_bwd_kv_splits(const mad_plan* p, int32_t Hq, int32_t Hkv, int32_t* splits) {
+  clear_error();
+  if (!p || !splits) return fail(MAD_ERR_INVALID, "mad_bwd_kv_splits: NULL argument");
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv) return fail(MAD_ERR_INVALID, "mad_bwd_kv_splits: Hq must be a positive multiple of Hkv");
+  if (Hq % p->G) return fail(MAD_ERR_INVALID, "mad_bwd_kv_splits: plan mask groups must divide Hq");
+  *splits = dkdv_splits(p, Hq, Hkv);
   return MAD_OK;
 }
 

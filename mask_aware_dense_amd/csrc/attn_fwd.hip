@@ -6,8 +6,9 @@
 // start from (section 1), under a compiled mask.  A row with no allowed key
 // gets O = 0, LSE = -inf.
 //
-// Work decomposition: one workgroup per (query head, 128-row query tile), two
-// wave64s of 64 rows each.  The workgroup walks the query tile's list of
+// Work decomposition: one workgroup per (query head, 128-row query tile), four
+// wave64s of 32 rows each (two workgroups per CU at head dim 64 / 128, so two
+// waves share each SIMD).  The workgroup walks the query tile's list of
 // non-EMPTY 64-key tiles.  K and V tiles reach LDS by direct global->LDS
 // loads into a double buffer: the loads of tile t+1 are issued right after
 // the barrier that opens tile t, so they overlap tile t's arithmetic and no

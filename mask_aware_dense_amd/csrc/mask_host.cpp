@@ -366,8 +366,19 @@ extern "C" mad_status mad_mask_slices(int32_t pattern, int32_t T, const mad_mask
                        pattern == MAD_MASK_CAUSAL_BLOCKWISE_LAST || pattern == MAD_MASK_BLOCK_CAUSAL_DOCUMENT_GLOBAL;
   if (blocked && P.block <= 0)
     return fail(MAD_ERR_INVALID, "mad_mask_slices: block must be > 0");
-  if (pattern == MAD_MASK_SHARED_QUESTION && (P.question < 0 || P.n_answers <= 0))
+  // SHARED_QUESTION: answers split the rest equally, or take the lengths given in doc_lens
+  const bool sq_lens = pattern == MAD_MASK_SHARED_QUESTION && P.doc_lens && P.n_docs > 0;
+  if (pattern == MAD_MASK_SHARED_QUESTION && (P.question < 0 || (!sq_lens && P.n_answers <= 0)))
     return fail(MAD_ERR_INVALID, "mad_mask_slices: question >= 0 and n_answers > 0 required");
+  if (sq_lens) {
+    int64_t sum = 0;
+    for (int32_t x = 0; x < P.n_docs; ++x) {
+      if (P.doc_lens[x] < 0) return fail(MAD_ERR_INVALID, "mad_mask_slices: negative answer length");
+      sum += P.doc_lens[x];
+    }
+    if (sum != T - std::min(P.question, T))
+      return fail(MAD_ERR_INVALID, "mad_mask_slices: answer lengths do not sum to T - question");
+  }
   if (pattern == MAD_MASK_GLOBAL_SLIDING && P.global_len < 0)
     return fail(MAD_ERR_INVALID, "mad_mask_slices: global_len must be >= 0");
 
@@ -422,11 +433,15 @@ extern "C" mad_status mad_mask_slices(int32_t pattern, int32_t T, const mad_mask
     case MAD_MASK_SHARED_QUESTION: {
       const int32_t Q = std::min(P.question, T);
       S.add(0, Q, 0, Q, C);
-      const int32_t rest = T - Q, base = rest / P.n_answers;
-      for (int32_t a = 0; a < P.n_answers; ++a) {
-        const int32_t a0 = Q + a * base, a1 = (a == P.n_answers - 1) ? T : a0 + base;
-        S.add(a0, a1, 0, Q, F);
-        S.add(a0, a1, a0, a1, C);
+      const int32_t rest = T - Q, na = sq_lens ? P.n_docs : P.n_answers, base = rest / na;
+      int32_t a0 = Q;
+      for (int32_t a = 0; a < na; ++a) {
+        const int32_t a1 = sq_lens ? a0 + P.doc_lens[a] : (a == na - 1) ? T : a0 + base;
+        if (a1 > a0) {
+          S.add(a0, a1, 0, Q, F);
+          S.add(a0, a1, a0, a1, C);
+        }
+        a0 = a1;
       }
       break;
     }

@@ -140,7 +140,41 @@ def attn_bwd(q, k, v, do, spec, scale, o=None, lse=None, heads=None,
     return {"dq": dq, "dk": dk, "dv": dv}
 
 
-def delta(o, do):
-    """D [Hq, Tq] = rowsum(dO * O) (the backward's pre-pass quantity)."""
-    o, do = to_f64(o), to_f64(do)
-    return np.einsum("thd,thd->ht", o, do)
+def attn_bwd_keys(q, k, v, do, spec, scale, keys, kv_heads=None):
+    """dK, dV at chosen key columns only: ([len(keys), len(kv_heads), d] each).
+
+    The same definition as attn_bwd restricted to the columns j in `keys`:
+    dK_j = scale * sum_{h in group} sum_i dS^h_ij q^h_i and
+    dV_j = sum_{h in group} sum_i P^h_ij dO^h_i.  Every query row of the
+    group's heads that sees one of the keys contributes; each such row's O
+    and LSE (hence P and D) come from the oracle's own forward over all of
+    that row's keys.  Rows that see none of the chosen keys contribute
+    nothing and are skipped.
+    """
+    q, k, v, do = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
+    Tq, Hq, d = q.shape
+    Hkv = k.shape[1]
+    R = Hq // Hkv
+    keys = np.asarray(keys, dtype=np.int64)
+    kv_heads = list(range(Hkv)) if kv_heads is None else list(kv_heads)
+    dk = np.zeros((len(keys), len(kv_heads), d))
+    dv = np.zeros((len(keys), len(kv_heads), d))
+    for gi, g in enumerate(kv_heads):
+        for h in range(g * R, (g + 1) * R):
+            mg = _mask_group(spec, h, Hq)
+            for r0 in range(0, Tq, ROW_BLOCK):
+                rr = np.arange(r0, min(Tq, r0 + ROW_BLOCK))
+                Mk = _masks.allowed(spec, rr, keys, mg)
+                sel = Mk.any(axis=1)
+                if not sel.any():
+                    continue
+                rs, Mk = rr[sel], Mk[sel]
+                ob, lb = fwd_rows(q, k, v, spec, scale, h, rs)  # every row here has a key, so lb is finite
+                S = scale * (q[rs, h, :] @ k[keys, g, :].T)
+                P = np.where(Mk, np.exp(np.where(Mk, S, 0.0) - lb[:, None]), 0.0)
+                dob = do[rs, h, :]
+                D = (dob * ob).sum(axis=1)
+                dS = P * (dob @ v[keys, g, :].T - D[:, None])
+                dk[:, gi, :] += scale * (dS.T @ q[rs, h, :])
+                dv[:, gi, :] += P.T @ dob
+    return dk, dv

@@ -19,7 +19,8 @@ Readings where the pages are silent (the library takes the same ones):
   * sliding window W counts the key itself: i-W < j <= i
   * Prefix LM prefix P = floor(T/4), bidirectional inside the prefix
   * Shared Question answers split the rest equally, the last takes the
-    remainder; the question is causal within itself
+    remainder, unless sampled answer lengths are given (the timing runs
+    sample them); the question is causal within itself
   * Global Sliding: keys 0..G-1 visible to every later query, no look-ahead
   * Causal Blockwise read literally (causal within a block, full to earlier
     blocks), which is the same set as CAUSAL
@@ -69,6 +70,7 @@ class MaskSpec:
     doc_lens: tuple = ()          # document variants
     question: int = 2048          # SHARED_QUESTION
     n_answers: int = 4
+    answer_lens: tuple = ()       # SHARED_QUESTION: sampled answer lengths (sum T - question) instead of equal
     global_len: int = 256         # GLOBAL_SLIDING
     block: int = 1024             # BLOCK_CAUSAL_DOCUMENT (1024), CAUSAL_BLOCKWISE (2048)
     # block-sparse: edges are cumulative boundaries (length n_blocks+1), keep is
@@ -103,8 +105,12 @@ def _doc_index(doc_lens, pos):
     return d, starts[d], np.asarray(doc_lens, dtype=np.int64)[d]
 
 
-def _answer_segment(T, question, n_answers, pos):
-    """Segment id: 0 for the question, 1..n for answers (equal split of the rest)."""
+def _answer_segment(T, question, n_answers, pos, answer_lens=()):
+    """Segment id: 0 for the question, 1..n for answers (equal split of the rest, or the given
+    answer lengths, which sum to T - question)."""
+    if len(answer_lens):
+        ends = question + np.cumsum(np.asarray(answer_lens, dtype=np.int64))
+        return np.where(pos < question, 0, np.searchsorted(ends, pos, side="right") + 1)
     rest = T - question
     base = rest // n_answers
     a = pos - question
@@ -192,8 +198,8 @@ def allowed(spec: MaskSpec, rows, cols, group: int = 0) -> np.ndarray:
         return j <= np.maximum(i, P - 1)
     if p == "SHARED_QUESTION":
         Q = spec.question
-        si = _answer_segment(T, Q, spec.n_answers, i)
-        sj = _answer_segment(T, Q, spec.n_answers, j)
+        si = _answer_segment(T, Q, spec.n_answers, i, spec.answer_lens)
+        sj = _answer_segment(T, Q, spec.n_answers, j, spec.answer_lens)
         return (j <= i) & ((j < Q) | (si == sj))
     if p == "GLOBAL_SLIDING":
         G, W = spec.global_len, spec.window

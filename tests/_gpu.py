@@ -20,8 +20,10 @@ def spec_kwargs(spec):
               global_len=spec.global_len, block=spec.block)
     if spec.prefix is not None:
         kw["prefix"] = spec.prefix
-    if spec.doc_lens:
+    if spec.doc_lens and spec.pattern != "SHARED_QUESTION":  # the C ABI reads doc_lens as answer lengths there
         kw["doc_lens"] = list(spec.doc_lens)
+    if spec.answer_lens:
+        kw["answer_lens"] = list(spec.answer_lens)
     return kw
 
 

@@ -70,15 +70,21 @@ def test_compile_errors():
 
 
 class _Fake:
-    """Stand-in tensor: shape, strides and a (never dereferenced) address."""
+    """Stand-in GPU tensor: shape, strides, dtype, device and a (never dereferenced) address."""
 
-    def __init__(self, shape, addr=4096):
+    def __init__(self, shape, addr=4096, dtype=None, device=None, contiguous=True):
+        import torch
         self.shape = shape
         self._addr = addr
         st = [1] * len(shape)
         for i in range(len(shape) - 2, -1, -1):
             st[i] = st[i + 1] * shape[i + 1]
         self._st = st
+        if dtype is None:
+            dtype = torch.float32 if len(shape) == 2 else torch.bfloat16 if len(shape) == 3 else torch.uint8
+        self.dtype = dtype
+        self.device = torch.device("cuda", 0) if device is None else device
+        self._contig = contiguous
 
     def stride(self, i):
         return self._st[i]
@@ -92,6 +98,9 @@ class _Fake:
     def element_size(self):
         return 1
 
+    def is_contiguous(self):
+        return self._contig
+
 
 def test_attention_argument_errors_launch_nothing():
     """Every check below fails before any HIP call (no GPU in this container)."""
@@ -100,13 +109,14 @@ def test_attention_argument_errors_launch_nothing():
     q, k, v = _Fake((T, 4, 128)), _Fake((T, 2, 128)), _Fake((T, 2, 128))
     o, lse = _Fake((T, 4, 128)), _Fake((4, T))
     with pytest.raises(mad.MadError) as e:
-        mad.attn_fwd(plan, _Fake((T, 4, 96)), _Fake((T, 2, 96)), _Fake((T, 2, 96)), o, lse, 0.1, stream=0)
+        mad.attn_fwd(plan, _Fake((T, 4, 96)), _Fake((T, 2, 96)), _Fake((T, 2, 96)), _Fake((T, 4, 96)), lse, 0.1,
+                     stream=0)
     assert _status(e) == 2  # head dim
     with pytest.raises(mad.MadError) as e:
-        mad.attn_fwd(plan, _Fake((T, 3, 128)), k, v, o, lse, 0.1, stream=0)
+        mad.attn_fwd(plan, _Fake((T, 3, 128)), k, v, _Fake((T, 3, 128)), _Fake((3, T)), 0.1, stream=0)
     assert _status(e) == 1  # Hq % Hkv
     with pytest.raises(mad.MadError) as e:
-        mad.attn_fwd(plan, _Fake((T + 1, 4, 128)), k, v, o, lse, 0.1, stream=0)
+        mad.attn_fwd(plan, _Fake((T + 1, 4, 128)), k, v, _Fake((T + 1, 4, 128)), _Fake((4, T + 1)), 0.1, stream=0)
     assert _status(e) == 1 and "compiled for" in str(e.value)
     with pytest.raises(mad.MadError) as e:
         mad.attn_fwd(plan, q, k, v, o, lse, 0.1, stream=0)
@@ -222,3 +232,47 @@ def test_probe_mfma_errors():
     assert L.mad_probe_mfma(0, 10, ctypes.c_void_p(4096), None) == 1
     assert L.mad_probe_mfma(4, 0, ctypes.c_void_p(4096), None) == 1
     assert L.mad_probe_mfma(4, 10, None, None) == 1
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The binding checks dtypes, exact shapes, one device and packed layouts before calling the
+    library: the kernels address o, d_o, dq, dk, dv and lse as packed tensors."""
+    import torch
+    T, Hq, Hkv, d = 64, 4, 2, 128
+    plan = mad.mask_compile(mad.mask_slices("CAUSAL", T), T, T)
+    q, k, v = _Fake((T, Hq, d)), _Fake((T, Hkv, d)), _Fake((T, Hkv, d))
+    o, lse = _Fake((T, Hq, d)), _Fake((Hq, T))
+    ws = _Fake((1 << 16,))
+
+    def fwd(**over):
+        a = dict(q=q, k=k, v=v, o=o, lse=lse)
+        a.update(over)
+        with pytest.raises(mad.MadError) as e:
+            mad.attn_fwd(plan, a["q"], a["k"], a["v"], a["o"], a["lse"], 0.1, stream=0)
+        return str(e.value)
+
+    def bwd(**over):
+        a = dict(q=q, k=k, v=v, o=o, d_o=_Fake((T, Hq, d)), lse=lse, dq=_Fake((T, Hq, d)), dk=_Fake((T, Hkv, d)),
+                 dv=_Fake((T, Hkv, d)), ws=ws)
+        a.update(over)
+        with pytest.raises(mad.MadError) as e:
+            mad.attn_bwd(plan, a["q"], a["k"], a["v"], a["o"], a["d_o"], a["lse"], a["dq"], a["dk"], a["dv"], a["ws"],
+                         0.1, stream=0)
+        return str(e.value)
+
+    assert "q must be bfloat16" in fwd(q=_Fake((T, Hq, d), dtype=torch.float32))
+    assert "v shape" in fwd(v=_Fake((T, 1, d)))
+    assert "o must have shape" in fwd(o=_Fake((T - 1, Hq, d)))
+    assert "o must be bfloat16" in fwd(o=_Fake((T, Hq, d), dtype=torch.float16))
+    assert "o must be contiguous" in fwd(o=_Fake((T, Hq, d), contiguous=False))
+    assert "lse must have shape" in fwd(lse=_Fake((T, Hq)))
+    assert "lse must be float32" in fwd(lse=_Fake((Hq, T), dtype=torch.bfloat16))
+    assert "is on cpu" in fwd(o=_Fake((T, Hq, d), device=torch.device("cpu")))
+    assert "k is on cuda:1" in fwd(k=_Fake((T, Hkv, d), device=torch.device("cuda", 1)))
+    assert "dk must have shape" in bwd(dk=_Fake((T, Hq, d)))
+    assert "dv must be contiguous" in bwd(dv=_Fake((T, Hkv, d), contiguous=False))
+    assert "d_o must be bfloat16" in bwd(d_o=_Fake((T, Hq, d), dtype=torch.float32))
+    assert "dq must not be None" in bwd(dq=None)
+    assert "workspace must be a contiguous GPU tensor" in bwd(ws=_Fake((256,), device=torch.device("cpu")))
+    # a correct call still reaches the library's own checks (the plan is not uploaded)
+    assert "not uploaded" in bwd()

@@ -165,3 +165,17 @@ def test_sparse_all_kept_equals_full():
     for w in (0, 1):  # the dK/dV tilings differ in width (64-token blocks): every tile is FULL in both
         assert np.all(a.export(w)["classes"] == 1) and np.all(b.export(w)["classes"] == 1)
     assert int(a.stats()["pairs"][0]) == T * T
+
+
+@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("T", [777, 4096])
+def test_shared_question_sampled_answers_bit_exact(T, seed):
+    """Shared Question with sampled answer lengths (some possibly empty)."""
+    from mad_inputs import answer_lengths
+    Q = T // 8
+    lens = tuple(int(x) for x in answer_lengths(seed, T - Q, 4))
+    spec = M.MaskSpec("SHARED_QUESTION", T, T, question=Q, answer_lens=lens)
+    plan = mad.mask_compile(mad.mask_slices("SHARED_QUESTION", T, question=Q, answer_lens=lens), T, T)
+    _assert_plan_matches(plan, spec)
+    with pytest.raises(mad.MadError):
+        mad.mask_slices("SHARED_QUESTION", T, question=Q, answer_lens=[1, 2])

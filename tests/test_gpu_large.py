@@ -125,3 +125,29 @@ def test_ring_step_full_shape():
     sl = mad.ring_step_slices("headtail", 12, C, 0, 0)
     q, k, v, do, scale, got = _full_run(spec, 64, 8, 128, seed=4, sl=sl)
     _check_sampled(spec, q, k, v, do, scale, got, n_rows=24, heads=[0, 9, 63])
+
+
+def _check_keys(spec, q, k, v, do, scale, got, kv_head, keys):
+    """dK / dV of one KV head at chosen key columns, element by element against the oracle (every
+    query row of the group's heads that sees one of the keys; process pool over those heads)."""
+    import _pool
+    dk, dv = _pool.oracle_keys(q, k, v, do, spec, scale, keys, kv_head)
+    _gpu.check_close("dk", got["dk"][keys, kv_head], dk, _gpu.TOL_BWD)
+    _gpu.check_close("dv", got["dv"][keys, kv_head], dv, _gpu.TOL_BWD)
+
+
+@pytest.mark.parametrize("pattern", ["FULL", "SLIDING_WINDOW", "PREFIX_LM", "CAUSAL_BLOCKWISE", "PREFIX_LM_DOCUMENT"])
+def test_32k_gqa_64_8_patterns(pattern):
+    """Static patterns at the suite's 32K GQA 64:8 shape and parameters (4K window, 25% prefix, 2K
+    blocks, documents log-uniform in [512, 16K]): sampled rows of O, LSE, dQ, and dK / dV of one KV
+    head at sampled keys (tile edges, the first and last key, and random ones)."""
+    T = 32768
+    docs = tuple(int(x) for x in doc_lengths(13, T))
+    spec = M.MaskSpec(pattern, T, T, window=4096, block=2048, doc_lens=docs)
+    q, k, v, do, scale, got = _full_run(spec, 64, 8, 128, seed=31)
+    _check_sampled(spec, q, k, v, do, scale, got, n_rows=24, seed=3, heads=[0, 21, 63])
+    rng = np.random.default_rng(7)
+    keys = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 8191, 8192, 16383, 32767],
+                                     rng.choice(T, size=6, replace=False)]))
+    _check_keys(spec, q, k, v, do, scale, got, kv_head=5, keys=keys)
+    _check_bwd_invariants(got, do, np.ones((T, 64), bool), 8)

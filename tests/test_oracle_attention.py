@@ -49,13 +49,18 @@ def _allowed_fn(spec, Hq):
     return f
 
 
-@pytest.mark.parametrize("idx", range(20))
+N_TINY = len(all_tiny_specs(16))
+
+
+def test_every_tiny_spec_is_brute_forced():
+    """The brute-force tests below cover every tiny spec, at both sizes."""
+    assert N_TINY == len(all_tiny_specs(24)) == 22
+
+
+@pytest.mark.parametrize("idx", range(N_TINY))
 def test_fwd_matches_brute_force(idx):
     T, Hq, Hkv, d = 24, 4, 2, 5
-    specs = all_tiny_specs(T)
-    if idx >= len(specs):
-        pytest.skip("no case")
-    spec = specs[idx]
+    spec = all_tiny_specs(T)[idx]
     q, k, v = rnd(idx, T, Hq, d), rnd(100 + idx, T, Hkv, d), rnd(200 + idx, T, Hkv, d)
     scale = 0.7
     O, L = A.attn_fwd(q, k, v, spec, scale)
@@ -67,13 +72,10 @@ def test_fwd_matches_brute_force(idx):
     assert np.max(np.abs(L[fin] - Lb[fin]), initial=0.0) < 1e-12, spec.pattern
 
 
-@pytest.mark.parametrize("idx", range(20))
+@pytest.mark.parametrize("idx", range(N_TINY))
 def test_bwd_matches_brute_force(idx):
     T, Hq, Hkv, d = 16, 4, 2, 3
-    specs = all_tiny_specs(T)
-    if idx >= len(specs):
-        pytest.skip("no case")
-    spec = specs[idx]
+    spec = all_tiny_specs(T)[idx]
     q, k, v, do = rnd(idx, T, Hq, d), rnd(50 + idx, T, Hkv, d), rnd(60 + idx, T, Hkv, d), rnd(70 + idx, T, Hq, d)
     scale = 0.9
     g = A.attn_bwd(q, k, v, do, spec, scale)
@@ -317,3 +319,28 @@ def test_sampled_rows_match_full():
     g = A.attn_bwd(q, k, v, do, spec, 0.5)
     gs = A.attn_bwd(q, k, v, do, spec, 0.5, rows=rows, want=("dq",))
     assert np.max(np.abs(g["dq"][rows] - gs["dq"])) < 1e-13
+
+
+@pytest.mark.parametrize("idx", range(N_TINY))
+def test_bwd_keys_match_brute_force(idx):
+    """dK / dV at chosen key columns equal the pure-Python brute force at those columns."""
+    T, Hq, Hkv, d = 16, 4, 2, 3
+    spec = all_tiny_specs(T)[idx]
+    q, k, v, do = rnd(idx, T, Hq, d), rnd(50 + idx, T, Hkv, d), rnd(60 + idx, T, Hkv, d), rnd(70 + idx, T, Hq, d)
+    keys = np.array([0, 3, 7, 8, 15])
+    dk, dv = A.attn_bwd_keys(q, k, v, do, spec, 0.9, keys)
+    _, bdk, bdv = _brute.bwd(nested(q), nested(k), nested(v), nested(do), _allowed_fn(spec, Hq), 0.9)
+    assert np.max(np.abs(dk - np.array(bdk)[keys])) < 1e-11, spec.pattern
+    assert np.max(np.abs(dv - np.array(bdv)[keys])) < 1e-11, spec.pattern
+
+
+@pytest.mark.parametrize("spec", small_specs(300, seed=6), ids=lambda s: s.pattern)
+def test_bwd_keys_match_full_backward(spec):
+    """Across several row blocks (T = 300 > ROW_BLOCK) and for one KV head of a GQA group."""
+    T, Hq, Hkv, d = 300, 4, 2, 8
+    q, k, v, do = rnd(11, T, Hq, d), rnd(12, T, Hkv, d), rnd(13, T, Hkv, d), rnd(14, T, Hq, d)
+    keys = np.array([0, 1, 77, 150, 255, 256, 299])
+    g = A.attn_bwd(q, k, v, do, spec, 0.35)
+    dk, dv = A.attn_bwd_keys(q, k, v, do, spec, 0.35, keys, kv_heads=[1])
+    assert np.max(np.abs(dk[:, 0] - g["dk"][keys, 1])) < 1e-12
+    assert np.max(np.abs(dv[:, 0] - g["dv"][keys, 1])) < 1e-12

@@ -357,3 +357,29 @@ def test_varlen_cross_attention_counts(lq, lk):
         seq2 = sum(min(lk, max(0, r + 1 + sh)) for r in range(lq))
         seq1 = sum(min(pre_k, max(0, r + 1 + ((pre_k - pre_q) if br else 0))) for r in range(pre_q))
         assert M.pair_count(spec) == seq1 + seq2
+
+
+def sq_pairs_lens(Q, lens):
+    return Q * (Q + 1) // 2 + sum(L * Q + L * (L + 1) // 2 for L in lens)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_shared_question_sampled_answers(seed):
+    """Sampled answer lengths (the timing runs' Shared Question samples): the pair count follows
+    from the lengths; lengths equal to the equal split give the default mask; a single answer of
+    the whole rest gives CAUSAL."""
+    from mad_inputs import answer_lengths
+    T, Q = 3000, 512
+    lens = tuple(int(x) for x in answer_lengths(seed, T - Q, 4))
+    assert sum(lens) == T - Q and len(lens) == 4 and min(lens) >= 0
+    spec = M.MaskSpec("SHARED_QUESTION", T, T, question=Q, answer_lens=lens)
+    assert M.pair_count(spec) == sq_pairs_lens(Q, lens)
+    base = (T - Q) // 4
+    eq = (base, base, base, T - Q - 3 * base)
+    assert np.array_equal(M.dense(M.MaskSpec("SHARED_QUESTION", T, T, question=Q, answer_lens=eq)),
+                          M.dense(M.MaskSpec("SHARED_QUESTION", T, T, question=Q, n_answers=4)))
+    assert np.array_equal(M.dense(M.MaskSpec("SHARED_QUESTION", T, T, question=Q, answer_lens=(T - Q,))),
+                          M.dense(M.MaskSpec("CAUSAL", T, T)))
+    # an empty answer changes nothing for the others
+    z = (lens[0], 0, lens[1] + lens[2], lens[3])
+    assert M.pair_count(M.MaskSpec("SHARED_QUESTION", T, T, question=Q, answer_lens=z)) == sq_pairs_lens(Q, z)
