@@ -48,8 +48,12 @@ def _keys_task(args):
 def _run(fn, tasks):
     if len(tasks) == 1:
         return [fn(tasks[0])]
+    out = []
     with mp.get_context("spawn").Pool(n_workers(len(tasks))) as pool:
-        return pool.map(fn, tasks, chunksize=1)
+        for i, r in enumerate(pool.imap(fn, tasks, chunksize=1)):
+            out.append(r)
+            print(f"  oracle head task {i + 1}/{len(tasks)} done", flush=True)
+    return out
 
 
 def head_spec(spec, h, Hq):
