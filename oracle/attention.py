@@ -140,14 +140,15 @@ def attn_bwd(q, k, v, do, spec, scale, o=None, lse=None, heads=None,
     return {"dq": dq, "dk": dk, "dv": dv}
 
 
-def attn_bwd_keys(q, k, v, do, spec, scale, keys, kv_heads=None):
+def attn_bwd_keys(q, k, v, do, spec, scale, keys, kv_heads=None, rows=None):
     """dK, dV at chosen key columns only: ([len(keys), len(kv_heads), d] each).
 
     The same definition as attn_bwd restricted to the columns j in `keys`:
     dK_j = scale * sum_{h in group} sum_i dS^h_ij q^h_i and
     dV_j = sum_{h in group} sum_i P^h_ij dO^h_i.  Every query row of the
-    group's heads that sees one of the keys contributes; each such row's O
-    and LSE (hence P and D) come from the oracle's own forward over all of
+    group's heads that sees one of the keys contributes (only the rows in
+    `rows`, if given: the sums split over disjoint row sets); each such row's
+    O and LSE (hence P and D) come from the oracle's own forward over all of
     that row's keys.  Rows that see none of the chosen keys contribute
     nothing and are skipped.
     """
@@ -162,8 +163,9 @@ def attn_bwd_keys(q, k, v, do, spec, scale, keys, kv_heads=None):
     for gi, g in enumerate(kv_heads):
         for h in range(g * R, (g + 1) * R):
             mg = _mask_group(spec, h, Hq)
-            for r0 in range(0, Tq, ROW_BLOCK):
-                rr = np.arange(r0, min(Tq, r0 + ROW_BLOCK))
+            rows_all = np.arange(Tq) if rows is None else np.asarray(rows, dtype=np.int64)
+            for r0 in range(0, len(rows_all), ROW_BLOCK):
+                rr = rows_all[r0:r0 + ROW_BLOCK]
                 Mk = _masks.allowed(spec, rr, keys, mg)
                 sel = Mk.any(axis=1)
                 if not sel.any():

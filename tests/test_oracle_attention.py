@@ -344,3 +344,8 @@ def test_bwd_keys_match_full_backward(spec):
     dk, dv = A.attn_bwd_keys(q, k, v, do, spec, 0.35, keys, kv_heads=[1])
     assert np.max(np.abs(dk[:, 0] - g["dk"][keys, 1])) < 1e-12
     assert np.max(np.abs(dv[:, 0] - g["dv"][keys, 1])) < 1e-12
+    # the contributions of disjoint row sets add up to the whole
+    parts = [A.attn_bwd_keys(q, k, v, do, spec, 0.35, keys, kv_heads=[1], rows=r)
+             for r in (np.arange(0, 130), np.arange(130, 300))]
+    assert np.max(np.abs(parts[0][0] + parts[1][0] - dk)) < 1e-12
+    assert np.max(np.abs(parts[0][1] + parts[1][1] - dv)) < 1e-12
