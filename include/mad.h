@@ -358,6 +358,27 @@ mad_status mad_attn_bwd(const mad_plan* plan, const void* q, const void* k, cons
                         int32_t Tk, int32_t Hq, int32_t Hkv, int32_t d, const int64_t* strides,
                         float scale, hipStream_t stream);
 
+/* The same backward with no workspace argument and no allocation of any kind,
+ * for callers that cannot allocate device memory around the call: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * The workspace is a static device array of MAD_STATIC_WORKSPACE_BYTES
+ * (64 MiB) built into the library: every GPU the library runs on holds its own
+ * copy from the library's first use on that device until the process ends.
+ * Calls that need more workspace than that (mad_bwd_workspace_bytes: about
+ * 8 bytes per query row and head, plus the fp32 dK / dV sums of cut columns)
+ * return MAD_ERR_UNSUPPORTED before anything is launched.  Every call on one
+ * GPU shares that GPU's array, which keeps the last call's contents (the
+ * kernels rewrite or zero every byte they read, so stale contents do not
+ * matter): calls that overlap on one GPU -- on different streams, or from
+ * different threads -- race on it and must be serialised by the caller.
+ * Arguments, outputs and errors as for mad_attn_bwd; the first call on a
+ * device looks up the array's device address (MAD_ERR_HIP on failure). */
+#define MAD_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+mad_status mad_attn_bwd_static(const mad_plan* plan, const void* q, const void* k, const void* v,
+                               const void* o, const void* d_o, const float* lse, void* dq, void* dk,
+                               void* dv, int32_t Tq, int32_t Tk, int32_t Hq, int32_t Hkv, int32_t d,
+                               const int64_t* strides, float scale, hipStream_t stream);
+
 /* The same backward, restricted to a subset of its three launches:
  * phases is a bit set of MAD_BWD_DELTA (the delta pre-pass), MAD_BWD_DKDV and
  * MAD_BWD_DQ (which read the workspace's delta rows).  Calling the three

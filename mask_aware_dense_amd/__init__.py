@@ -17,6 +17,7 @@ import numpy as np
 __all__ = [
     "MadError", "lib", "Plan", "mask_slices", "ring_step_slices", "varlen_slices", "block_topk", "sparse_plan_device",
     "mask_compile", "sparse_plan", "attn_fwd", "attn_bwd", "attn_bwd_phases", "bwd_workspace_bytes", "bwd_kv_splits",
+    "attn_bwd_static", "STATIC_WORKSPACE_BYTES",
     "block_mask", "block_mask_workspace_bytes", "lse_merge", "Ring", "BWD_DELTA", "BWD_DKDV", "BWD_DQ", "BWD_ALL",
     "PATTERNS", "SLICE_DTYPE",
 ]
@@ -81,6 +82,8 @@ _SIGS = {
                             _I32, _I32, _I32, _I32, _I32, _VP, _F32, _VP]),
     "mad_attn_bwd_phases": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
                                    _I32, _I32, _I32, _I32, _I32, _VP, _F32, ctypes.c_uint32, _VP]),
+    "mad_attn_bwd_static": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                   _I32, _I32, _I32, _I32, _I32, _VP, _F32, _VP]),
     "mad_block_mask_workspace_bytes": (_I32, [_I32, _I32, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)]),
     "mad_block_mask": (_I32, [_VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _I32, _VP, _I32, _I32, _F32,
                               _VP, ctypes.c_size_t, _VP, _VP, _VP]),
@@ -381,6 +384,21 @@ def attn_bwd(plan: Plan, q, k, v, o, d_o, lse, dq, dk, dv, workspace, scale: flo
     _check(lib().mad_attn_bwd(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
                               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes, Tq, Tk, Hq, Hkv, d,
                               st, float(scale), _stream(stream)))
+
+
+STATIC_WORKSPACE_BYTES = 64 << 20
+
+
+def attn_bwd_static(plan: Plan, q, k, v, o, d_o, lse, dq, dk, dv, scale: float, stream=None):
+    """Backward with the library's static device workspace (no workspace argument, no allocation)."""
+    Tq, Hq, d = q.shape
+    Tk, Hkv, _ = k.shape
+    _check_tensors(q, k, v, {"o": (o, (Tq, Hq, d)), "d_o": (d_o, (Tq, Hq, d)), "dq": (dq, (Tq, Hq, d)),
+                             "dk": (dk, (Tk, Hkv, d)), "dv": (dv, (Tk, Hkv, d))}, lse)
+    st = _qkv_strides(q, k, v)
+    _check(lib().mad_attn_bwd_static(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
+                                     _ptr(dq), _ptr(dk), _ptr(dv), Tq, Tk, Hq, Hkv, d, st, float(scale),
+                                     _stream(stream)))
 
 
 def attn_bwd_phases(plan: Plan, q, k, v, o, d_o, lse, dq, dk, dv, workspace, scale: float, phases: int,

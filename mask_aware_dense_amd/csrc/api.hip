@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "kernel_common.hpp"
@@ -371,4 +372,65 @@ extern "C" mad_status mad_attn_bwd(const mad_plan* p, const void* q, const void*
                                    const int64_t* strides, float scale, hipStream_t stream) {
   return mad_attn_bwd_phases(p, q, k, v, o, d_o, lse, dq, dk, dv, workspace, ws_bytes, Tq, Tk, Hq, Hkv, d, strides,
                              scale, MAD_BWD_ALL, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The backward without a caller workspace, for callers that cannot allocate
+// device memory (code under HIP graph capture, tight serving loops, hosts that
+// forbid allocation in the step).  Its workspace is this file-scope device
+// array: each GPU the library runs on holds one copy, at its own address, from
+// the code object's load until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the device
+// symbol): the device address comes from hipGetSymbolAddress, taken once per
+// device with that device current and kept in scratch_dev.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[MAD_STATIC_WORKSPACE_BYTES];
+
+namespace mad {
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];  // device address of `scratch` on each device (null: not looked up yet)
+
+mad_status scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(MAD_ERR_UNSUPPORTED, "mad_attn_bwd_static: device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return fail(MAD_ERR_HIP, std::string("mad_attn_bwd_static: hipGetSymbolAddress: ") + hipGetErrorString(e));
+    }
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return MAD_OK;
+}
+}  // namespace
+}  // namespace mad
+
+extern "C" mad_status mad_attn_bwd_static(const mad_plan* p, const void* q, const void* k, const void* v,
+                                          const void* o, const void* d_o, const float* lse, void* dq, void* dk,
+                                          void* dv, int32_t Tq, int32_t Tk, int32_t Hq, int32_t Hkv, int32_t d,
+                                          const int64_t* strides, float scale, hipStream_t stream) {
+  clear_error();
+  if (!p) return fail(MAD_ERR_INVALID, "mad_attn_bwd_static: plan is NULL");
+  if (!p->dev_mem) return fail(MAD_ERR_INVALID, "mad_attn_bwd_static: plan not uploaded (call mad_plan_upload)");
+  size_t need = 0;
+  mad_status s = mad_bwd_workspace_bytes(p, Tq, Tk, Hq, Hkv, d, &need);
+  if (s != MAD_OK) return s;
+  if (need > MAD_STATIC_WORKSPACE_BYTES)
+    return fail(MAD_ERR_UNSUPPORTED, "mad_attn_bwd_static: this call needs " + std::to_string(need) +
+                                         " bytes of workspace, more than the " +
+                                         std::to_string((size_t)MAD_STATIC_WORKSPACE_BYTES) +
+                                         "-byte static workspace; use mad_attn_bwd with a caller workspace");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("mad_attn_bwd_static", e);
+  void* ws = nullptr;
+  s = scratch_address(dev, &ws);
+  if (s != MAD_OK) return s;
+  return attn_bwd_impl(p, q, k, v, o, d_o, lse, dq, nullptr, dk, dv, ws, MAD_STATIC_WORKSPACE_BYTES, Tq, Tk, Hq, Hkv,
+                       d, strides, scale, MAD_BWD_ALL, stream);
 }
