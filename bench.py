@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--d", type=int, default=128)
     ap.add_argument("--mask", default="CAUSAL")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-rows", type=int, default=512, help="query rows in the oracle's timed sample")
+    ap.add_argument("--cpu-rows", type=int, default=1024, help="query rows in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fwd-only", action="store_true", help="time only the forward (profiling aid)")
     ap.add_argument("--suite", action="store_true", help="run every workload family, one JSON line each")
@@ -612,9 +612,11 @@ def _alloc_bytes(t) -> int:
 
 def peak_memory_case(torch, mad, mask, T, Hq, Hkv, d, seed, kw=None):
     """Peak device memory of one forward and one forward+backward (appendix A.4.2): torch's allocator
-    peak over the call's live tensors plus the plan's device block, with the sum those tensors and the
-    plan should come to if the library allocates nothing else, and the free device memory before and
-    after the calls (unchanged if nothing is left allocated)."""
+    peak over the call's live tensors plus the plan's device block; beside it the allocator's count of
+    the live tensors just before each call (equal to the peak if the call allocates nothing through
+    torch), the tensors' own sizes (the allocator rounds each block up, by at most a segment
+    remainder), and the free device memory before and after each call (unchanged if the library
+    allocates nothing)."""
     from mad_inputs import grad_out, qkv
     dev = torch.device("cuda", 0)
     torch.cuda.synchronize()
@@ -629,6 +631,7 @@ def peak_memory_case(torch, mad, mask, T, Hq, Hkv, d, seed, kw=None):
     lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
     scale = 1.0 / np.sqrt(d)
     torch.cuda.synchronize()
+    live_f = torch.cuda.memory_allocated() - base  # the forward's tensors as the allocator counts them
     free0 = torch.cuda.mem_get_info()[0]
     mad.attn_fwd(plan, q, k, v, o, lse, scale)
     torch.cuda.synchronize()
@@ -639,6 +642,7 @@ def peak_memory_case(torch, mad, mask, T, Hq, Hkv, d, seed, kw=None):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(mad.bwd_workspace_bytes(plan, T, T, Hq, Hkv, d), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
+    live_b = torch.cuda.memory_allocated() - base
     free1 = torch.cuda.mem_get_info()[0]
     mad.attn_bwd(plan, q, k, v, o, do, lse, dq, dk, dv, ws, scale)
     torch.cuda.synchronize()
@@ -646,6 +650,7 @@ def peak_memory_case(torch, mad, mask, T, Hq, Hkv, d, seed, kw=None):
     bwd_sum = fwd_sum + sum(_alloc_bytes(t) for t in (do, dq, dk, dv, ws))
     free2 = torch.cuda.mem_get_info()[0]
     rec = {"fwd_peak_bytes": int(fwd_peak), "fwdbwd_peak_bytes": int(bwd_peak), "plan_device_bytes": int(pb),
+           "fwd_live_plus_plan_bytes": int(live_f + pb), "fwdbwd_live_plus_plan_bytes": int(live_b + pb),
            "fwd_tensors_plus_plan_bytes": int(fwd_sum), "fwdbwd_tensors_plus_plan_bytes": int(bwd_sum),
            "free_bytes_change_fwd": int(free0) - int(free_f),
            "free_bytes_change_bwd": int(free1) - int(free2),

@@ -1,8 +1,9 @@
 """Peak device memory of the path (LongCA-bench appendix A.4.2, the pages' second metric): the
-forward's and the forward+backward's peaks equal exactly the bytes of the call's own tensors
-(inputs, outputs, backward workspace) plus the plan's device block -- the kernels allocate nothing
--- so the peak grows linearly in T, where the pages' model of a standard attention module,
-11bshd + 5bhs^2 + 2bshd, grows with T^2."""
+forward's and the forward+backward's peaks equal the call's own tensors (inputs, outputs, backward
+workspace, as the allocator counts their blocks) plus the plan's device block, and the free device
+memory is the same before and after each call -- the kernels allocate nothing -- so the peak grows
+linearly in T, where the pages' model of a standard attention module, 11bshd + 5bhs^2 + 2bshd,
+grows with T^2."""
 import os
 import sys
 
@@ -25,8 +26,15 @@ def test_peak_equals_tensors_plus_plan(mask, Hq, Hkv, kw):
     for n, T in enumerate((2048, 2048, 8192)):
         print(f"case peak memory {mask} T={T} {Hq}:{Hkv}", flush=True)
         r = bench.peak_memory_case(torch, mad, mask, T, Hq, Hkv, 128, seed=0, kw=kw)
-        assert r["fwd_peak_bytes"] == r["fwd_tensors_plus_plan_bytes"], r
-        assert r["fwdbwd_peak_bytes"] == r["fwdbwd_tensors_plus_plan_bytes"], r
+        print(r, flush=True)
+        # the peak is the live tensors plus the plan: nothing transient is allocated by the calls
+        assert r["fwd_peak_bytes"] == r["fwd_live_plus_plan_bytes"], r
+        assert r["fwdbwd_peak_bytes"] == r["fwdbwd_live_plus_plan_bytes"], r
+        # and the live blocks are the tensors themselves (the allocator rounds a block up by less than
+        # a 2 MiB segment: 9 tensors at most)
+        for ph in ("fwd", "fwdbwd"):
+            extra = r[f"{ph}_peak_bytes"] - r[f"{ph}_tensors_plus_plan_bytes"]
+            assert 0 <= extra <= 9 * (2 << 20), (ph, r)
         if n > 0:  # the first calls may load code objects; later ones must leave free memory unchanged
             assert r["free_bytes_change_fwd"] == 0 and r["free_bytes_change_bwd"] == 0, r
         recs[T] = r
