@@ -31,6 +31,107 @@
 
 namespace mad {
 
+// The items one dK/dV workgroup visits: (query head e of its KV group g,
+// position `it` in that head's visit list for key tile kt), as two cursors --
+// the item being computed and the next one, whose tiles are prefetched.  When
+// every query head of the group uses the same mask group (hence the same
+// list), the list is walked from its end with the heads innermost: all
+// workgroups then start at the last query tile and move down through the same
+// tiles at the same pace, so the workgroups running together read the same
+// Q / dO tiles and share them in L2 (walking up from each key tile's first
+// tile would spread them apart).  Otherwise each head's list is walked in
+// turn.  With S = kv_splits > 1 the column's items are cut into S contiguous
+// chunks, one per workgroup (a few very long columns -- key tiles every query
+// sees, as under GLOBAL_SLIDING -- would otherwise set the kernel's length on
+// their own); the chunks' partial dK / dV are summed in fp32.
+struct KvCursor {
+  int e, it, end;  // shared list: `it` runs down to `end` (the list start)
+  int left;        // items of this workgroup's chunk still to visit
+  bool ok;
+};
+
+struct KvWalk {
+  const AttnParams& P;
+  int kt, h0, S, seg;
+  bool shared;
+  int n0, n1;  // this workgroup's chunk of the column's items
+
+  __device__ __forceinline__ KvWalk(const AttnParams& P_, int g, int kt_, int S_, int seg_)
+      : P(P_), kt(kt_), h0(g * P_.R), S(S_), seg(seg_), n0(0), n1(0) {
+    shared = (h0 / P.grp_div) == ((h0 + P.R - 1) / P.grp_div);
+  }
+  __device__ __forceinline__ void head_list(int e, KvCursor& cu) const {
+    const int32_t* ptr = P.t.ptr + (int64_t)((h0 + e) / P.grp_div) * (P.t.nmajor + 1);
+    cu.e = e;
+    cu.it = sld(ptr + kt);
+    cu.end = sld(ptr + kt + 1);
+  }
+  __device__ __forceinline__ void settle(KvCursor& cu) const {  // move past exhausted heads
+    while (cu.it >= cu.end && cu.e + 1 < P.R) head_list(cu.e + 1, cu);
+  }
+  __device__ __forceinline__ KvCursor first() {
+    KvCursor cu;
+    head_list(0, cu);
+    int ncol;
+    if (shared) {
+      ncol = P.R * (cu.end - cu.it);
+    } else {
+      ncol = 0;
+      for (int e = 0; e < P.R; ++e) {
+        KvCursor x;
+        head_list(e, x);
+        ncol += x.end - x.it;
+      }
+    }
+    n0 = (int)((int64_t)seg * ncol / S);
+    n1 = (int)((int64_t)(seg + 1) * ncol / S);
+    cu.left = n1 - n0;
+    if (shared) {
+      const int list_begin = cu.it;
+      cu.e = n0 % P.R;
+      cu.it = cu.end - 1 - n0 / P.R;
+      cu.end = list_begin;
+    } else {
+      int skip = n0;
+      settle(cu);
+      while (skip > 0) {
+        const int len = cu.end - cu.it;
+        if (len <= 0) break;  // lists exhausted (not reached: n0 < the column's item count)
+        if (skip < len) {
+          cu.it += skip;
+          skip = 0;
+        } else {
+          skip -= len;
+          cu.it = cu.end;
+          settle(cu);
+        }
+      }
+    }
+    cu.ok = cu.left > 0 && (shared || cu.it < cu.end);
+    return cu;
+  }
+  __device__ __forceinline__ KvCursor advance(KvCursor cu) const {
+    if (--cu.left <= 0) {
+      cu.ok = false;
+      return cu;
+    }
+    if (shared) {
+      if (cu.e + 1 < P.R) {
+        ++cu.e;
+      } else {
+        cu.e = 0;
+        --cu.it;
+      }
+      cu.ok = true;
+    } else {
+      ++cu.it;
+      settle(cu);
+      cu.ok = cu.it < cu.end;
+    }
+    return cu;
+  }
+};
+
 // At D = 256 each workgroup accumulates one 128-column half of dK / dV
 // (blockIdx.y), with S and dP still taken over all of D: K, V and both full
 // accumulators would not fit in a lane's 512 registers.
@@ -96,97 +197,7 @@ __global__ __launch_bounds__(64 * NW) void dkdv_kernel(const AttnParams P) {
     dva[db] = f32x16{};
   }
 
-  // Walk over the items (query head e of the group, position `it` in that
-  // head's visit list), kept as two cursors: the item being computed and the
-  // next one, whose tiles are prefetched.  When every query head of the group
-  // uses the same mask group (hence the same list), the list is walked from
-  // its end with the heads innermost: all workgroups then start at the last
-  // query tile and move down through the same tiles at the same pace, so the
-  // workgroups running together read the same Q / dO tiles and share them in
-  // L2 (walking up from each key tile's first tile would spread them apart).
-  // Otherwise each head's list is walked in turn.
-  // With kv_splits = S > 1 the column's items are cut into S contiguous
-  // chunks, one per workgroup (a few very long columns -- key tiles every
-  // query sees, as under GLOBAL_SLIDING -- would otherwise set the kernel's
-  // length on their own); the chunks' partial dK / dV are summed in fp32.
-  struct Cursor {
-    int e, it, end;  // shared list: `it` runs down to `end` (the list start)
-    int left;        // items of this workgroup's chunk still to visit
-    bool ok;
-  };
-  const int h0 = g * P.R;
-  const bool shared = (h0 / P.grp_div) == ((h0 + P.R - 1) / P.grp_div);
-  auto head_list = [&](int e, Cursor& cu) {
-    const int32_t* ptr = P.t.ptr + (int64_t)((h0 + e) / P.grp_div) * (P.t.nmajor + 1);
-    cu.e = e;
-    cu.it = sld(ptr + kt);
-    cu.end = sld(ptr + kt + 1);
-  };
-  auto settle = [&](Cursor& cu) {  // move past exhausted heads
-    while (cu.it >= cu.end && cu.e + 1 < P.R) head_list(cu.e + 1, cu);
-  };
-  int n0 = 0, n1 = 0;  // this workgroup's chunk of the column's items
-  auto first = [&]() {
-    Cursor cu;
-    head_list(0, cu);
-    int ncol;
-    if (shared) {
-      ncol = P.R * (cu.end - cu.it);
-    } else {
-      ncol = 0;
-      for (int e = 0; e < P.R; ++e) {
-        Cursor x;
-        head_list(e, x);
-        ncol += x.end - x.it;
-      }
-    }
-    n0 = (int)((int64_t)seg * ncol / S);
-    n1 = (int)((int64_t)(seg + 1) * ncol / S);
-    cu.left = n1 - n0;
-    if (shared) {
-      const int list_begin = cu.it;
-      cu.e = n0 % P.R;
-      cu.it = cu.end - 1 - n0 / P.R;
-      cu.end = list_begin;
-    } else {
-      int skip = n0;
-      settle(cu);
-      while (skip > 0) {
-        const int len = cu.end - cu.it;
-        if (len <= 0) break;  // lists exhausted (not reached: n0 < the column's item count)
-        if (skip < len) {
-          cu.it += skip;
-          skip = 0;
-        } else {
-          skip -= len;
-          cu.it = cu.end;
-          settle(cu);
-        }
-      }
-    }
-    cu.ok = cu.left > 0 && (shared || cu.it < cu.end);
-    return cu;
-  };
-  auto advance = [&](Cursor cu) {
-    if (--cu.left <= 0) {
-      cu.ok = false;
-      return cu;
-    }
-    if (shared) {
-      if (cu.e + 1 < P.R) {
-        ++cu.e;
-      } else {
-        cu.e = 0;
-        --cu.it;
-      }
-      cu.ok = true;
-    } else {
-      ++cu.it;
-      settle(cu);
-      cu.ok = cu.it < cu.end;
-    }
-    return cu;
-  };
+  KvWalk walk(P, g, kt, S, seg);
   const uint32_t smem_lds = lds_addr(smem), rowv_lds = lds_addr(&rowv[0][0]);
   TileLoader<D, KIND, NW, false> qload, dload;
   SwzRows srow;
@@ -197,7 +208,7 @@ __global__ __launch_bounds__(64 * NW) void dkdv_kernel(const AttnParams P) {
   }
   qload.init(P.q_tok, w, lane);
   dload.init((int64_t)P.Hq * D, w, lane);
-  auto issue = [&](const Cursor& cu, int buf) {
+  auto issue = [&](const KvCursor& cu, int buf) {
     const int hx = g * P.R + cu.e;
     const int q0 = (sld(P.t.ent + cu.it) & 0x7fffffff) * BM;
     qload.issue(smem_lds + (2 * buf) * TILE * 2, P.q + (int64_t)hx * P.q_head, P.q_tok, q0, P.Tq, w, lane);
@@ -211,7 +222,7 @@ __global__ __launch_bounds__(64 * NW) void dkdv_kernel(const AttnParams P) {
   // The K / V register loads complete before the first tiles are requested:
   // the loop's waits count the direct loads, which the compiler does not track.
   wait_vmem();
-  Cursor cur = first();
+  KvCursor cur = walk.first();
   if (cur.ok) issue(cur, 0);
 
   for (int n = 0; cur.ok; ++n) {
@@ -221,7 +232,7 @@ __global__ __launch_bounds__(64 * NW) void dkdv_kernel(const AttnParams P) {
     const uint32_t ent = (uint32_t)sld(P.t.ent + cur.it);
     const bool partial = (ent & ENT_PARTIAL) != 0;
     const int q0 = (int)(ent & 0x7fffffffu) * BM;
-    const Cursor nxt = advance(cur);
+    const KvCursor nxt = walk.advance(cur);
     wait_vmem();
     __syncthreads();
     // Rows of the tile this lane's key may see (PARTIAL tiles), evaluated
@@ -356,7 +367,7 @@ __global__ __launch_bounds__(64 * NW) void dkdv_kernel(const AttnParams P) {
 
   // dK, dV: lane holds column d = db*32 + li of key rows 8(r/4) + 4hh + r%4 of the wave's 32 keys.
   if (S > 1) {
-    if (n1 > n0) {
+    if (walk.n1 > walk.n0) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
