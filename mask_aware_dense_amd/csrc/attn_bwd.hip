@@ -177,16 +177,14 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void dq_kernel(const AttnPar
     const bf16* Ks = smem + buf * (KT + VT);
     const bf16* Vs = Ks + KT;
 
-    // Register r of key block kb holds key kb*32 + 16(r/8) + 8hh + r%8.
+    // Register r of key block kb holds key kb*32 + 16(r/8) + 8hh + r%8.  A
+    // block's first products start from an inline zero; masked (row, key)
+    // pairs get -inf once its scores are in, before P and dS are formed.
     f32x16 sc[2], dp[2];
-    auto init = [&](int kb) {  // at the start of key block kb, so only one block's scores are live
-      sc[kb] = f32x16{};
-      dp[kb] = f32x16{};
-      if (masked) {
+    auto apply_mask = [&](int kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (!((mbits[kb] >> (16 * (r >> 3) + 8 * hh + (r & 7))) & 1u)) sc[kb][r] = -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r)
+        if (!((mbits[kb] >> (16 * (r >> 3) + 8 * hh + (r & 7))) & 1u)) sc[kb][r] = -INFINITY;
     };
     bf16x8 opk[3], opv[3];
     auto ld1 = [&](int st) {
@@ -226,17 +224,17 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void dq_kernel(const AttnPar
     for (int u = 0; u < 2 * SPB; ++u) {
       if (u + 2 < 2 * SPB) load(u + 2);
       const int kb = u / SPB, v = u % SPB;
-      if (v == 0) init(kb);
       if (v < NKS) {
         const int p1 = kb * NKS + v;
-        sc[kb] = mfma32(opk[p1 % 3], qf[v], sc[kb]);
-        dp[kb] = mfma32(opv[p1 % 3], df[v], dp[kb]);
+        sc[kb] = mfma32(opk[p1 % 3], qf[v], v == 0 ? f32x16{} : sc[kb]);
+        dp[kb] = mfma32(opv[p1 % 3], df[v], v == 0 ? f32x16{} : dp[kb]);
       } else {
         const int j = v - NKS, p2 = kb * 2 * NDB + j;
         acc[j % NDB] = mfma32(trk[p2 % 3], sb[kb][j / NDB], acc[j % NDB]);
       }
       if (v == NKS - 1) {
         __builtin_amdgcn_sched_barrier(0);
+        if (__builtin_expect(masked, 0)) apply_mask(kb);
 #pragma unroll
         for (int r = 0; r < 16; r += 2) pds(kb, r);
       }

@@ -161,24 +161,18 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
     const bf16* Vs = Ks + KT;
     __builtin_amdgcn_sched_barrier(0);
 
-    // Scores start at 0, or at -inf on masked (row, key) pairs, so masking
-    // costs nothing past this initialisation.  Register r of s[kb][b] holds
-    // key kb*32 + 16(r/8) + 8hh + r%8 of row b*32 + li.
+    // Register r of s[kb][b] holds key kb*32 + 16(r/8) + 8hh + r%8 of row
+    // b*32 + li.  Each key block's first product starts from an inline zero
+    // (no register initialisation); masked (row, key) pairs are set to -inf
+    // once the block's products are in, just before its max is taken.
     f32x16 s[2][NB];
+    auto apply_mask = [&](int kb) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int b = 0; b < NB; ++b) s[kb][b] = f32x16{};
-    if (__builtin_expect(masked, 0)) {
-      asm volatile("" ::: "memory");
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (!((mbits[b][kb] >> (16 * (r >> 3) + 8 * hh + (r & 7))) & 1u)) s[kb][b][r] = -INFINITY;
-    }
+        for (int r = 0; r < 16; ++r)
+          if (!((mbits[b][kb] >> (16 * (r >> 3) + 8 * hh + (r & 7))) & 1u)) s[kb][b][r] = -INFINITY;
+    };
 
     // LDS operand rings, read two MFMA steps ahead.  Phase-1 step st = (kb,
     // ks): the K row operand; phase-2 step st = (kb, t2, db): the V^T operand.
@@ -195,7 +189,7 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
     auto s_step = [&](int st) {  // S^T of key block st / NKS, k-step st % NKS, both query blocks
       const int kb = st / NKS, ks = st % NKS;
 #pragma unroll
-      for (int b = 0; b < NB; ++b) s[kb][b] = mfma32(kr[st % 3], qf[b][ks], s[kb][b]);
+      for (int b = 0; b < NB; ++b) s[kb][b] = mfma32(kr[st % 3], qf[b][ks], ks == 0 ? f32x16{} : s[kb][b]);
     };
     bf16x8 pb[2][2][NB];  // P^T operands [kb][t2][b]
     auto pv_step = [&](int st) {  // O^T += V^T P^T for (kb, t2, db), both query blocks
@@ -261,6 +255,7 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
     }
     {
       float tmax[2];
+      if (__builtin_expect(masked, 0)) apply_mask(0);
       if (block_max(0, tmax)) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -301,6 +296,7 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
     bool resc1;
     {
       float tmax[2];
+      if (__builtin_expect(masked, 0)) apply_mask(1);
       resc1 = block_max(1, tmax);
       if (resc1) {
 #pragma unroll
