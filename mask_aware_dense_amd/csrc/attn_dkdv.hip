@@ -178,11 +178,6 @@ __global__ __launch_bounds__(64 * NW) void dkdv_kernel(const AttnParams P) {
   const int key = kt * BN + w * 32 + li;
   const int kc = min(key, P.Tk - 1);
   const float c = P.scale_log2;
-  // Key block of this lane's key, for the block-mask row reader (D <= 128:
-  // at D = 256 the extra live value costs that form registers, and it keeps
-  // the scalar walk).
-  constexpr bool BLKR = D <= 128;
-  const int kbj = BLKR && P.m.mode == MODE_BLOCKS ? P.m.col_kb[kc] : 0;
 
   // K, V of this lane's key as B operands: lane holds K[key][16ks + 8hh .. +8].
   bf16x8 kf[NKS], vf[NKS];
@@ -252,8 +247,7 @@ __global__ __launch_bounds__(64 * NW) void dkdv_kernel(const AttnParams P) {
     uint32_t mw[2] = {0u, 0u};
     if (masked) {
       const int k_lo = kt * BN + w * 32;  // the wave's keys, wave-uniform
-      const uint64_t rows = BLKR && P.m.mode == MODE_BLOCKS ? rowmask64_blocks(P.m, mg, key, kbj, q0)
-                                                            : rowmask64(P.m, aux, mg, key, q0, k_lo, k_lo + 31);
+      const uint64_t rows = rowmask64(P.m, aux, mg, key, q0, k_lo, k_lo + 31);
       mw[0] = (uint32_t)(rows >> (4 * hh));
       mw[1] = (uint32_t)(rows >> (32 + 4 * hh));
       wait_vmem();

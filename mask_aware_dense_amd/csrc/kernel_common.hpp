@@ -441,33 +441,6 @@ __device__ __forceinline__ uint64_t keymask64_blocks(const MaskDev& m, const uin
   }
   return bits;
 }
-// The same rows under a block mask (rowmask64's MODE_BLOCKS predicate), read
-// along key j's key block kbj (looked up once per workgroup): the tile's
-// query blocks are walked four at a time with their loads issued together
-// (edges as scalar loads, the lane's keep words as vector loads), instead of
-// a scalar walk over every (query block, key block) pair of the wave's keys.
-__device__ __forceinline__ uint64_t rowmask64_blocks(const MaskDev& m, int32_t grp, int j, int kbj, int row0) {
-  const int rlast = min(row0 + 63, m.Tq - 1);
-  if (j >= m.Tk || row0 > rlast) return 0ull;
-  uint64_t bits = 0ull;
-  const int qa = sld(m.row_qb + row0), qz = sld(m.row_qb + rlast);
-  const uint64_t* kcol = m.keep + (size_t)grp * m.n_qb * m.nw + (kbj >> 6);
-  const int sh = kbj & 63;
-  for (int q0 = qa; q0 <= qz; q0 += 4) {
-    int e[5];
-    uint64_t wd[4];
-#pragma unroll
-    for (int x = 0; x < 5; ++x) e[x] = sld(m.q_edges + min(q0 + x, m.n_qb));
-#pragma unroll
-    for (int x = 0; x < 4; ++x) wd[x] = kcol[(size_t)min(q0 + x, qz) * m.nw];
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-      if (q0 + x <= qz && ((wd[x] >> sh) & 1ull)) bits |= range_bits64(e[x] - row0, e[x + 1] - row0);
-  }
-  const int nvalid = m.Tq - row0;
-  if (nvalid < 64) bits &= (1ull << nvalid) - 1ull;
-  return bits;
-}
 // Allowed query rows among [row0, row0 + 64) for key j of a visited PARTIAL
 // tile of the dK/dV tiling, as a bitmask (bit r <-> row row0 + r): the same
 // predicate as keymask32, read along the key's column.  Rows >= Tq and keys
