@@ -73,10 +73,14 @@ def parse():
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources and the device build flags they are compiled with."""
+    from mask_aware_dense_amd import build as mad_build
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "mask_aware_dense_amd", "csrc", name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
+    dev_flags = [f.replace(mad_build.ROOT, "") for f in mad_build.flags()]  # no absolute paths
+    h.update(repr((dev_flags, sorted(mad_build.SOURCE_FLAGS.items()))).encode())
     return h.hexdigest()[:16]
 
 
