@@ -38,8 +38,8 @@ if ROOT not in sys.path:
 METRIC = "effective attention TFLOP/s fwd and fwd+bwd (unmasked FLOPs) vs bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_dkdv.hip", "ring.hip", "blockmask.hip", "kernel_common.hpp",
-                  "plan.hpp"]
+KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_dkdv.hip", "attn_dkdv.hpp", "attn_dkdv256.hip", "ring.hip",
+                  "blockmask.hip", "kernel_common.hpp", "plan.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 NAMES = ["fwd", "delta", "dkdv", "dq"]
 

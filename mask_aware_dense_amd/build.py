@@ -16,8 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmad.so")
-SOURCES = ["api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_dkdv.hip", "ring.hip", "blockmask.hip", "plan_gpu.hip",
-           "probe.hip", "mask_host.cpp"]
+SOURCES = ["api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_dkdv.hip", "attn_dkdv256.hip", "ring.hip", "blockmask.hip",
+           "plan_gpu.hip", "probe.hip", "mask_host.cpp"]
 ARCH = os.environ.get("MAD_OFFLOAD_ARCH", "gfx950")
 
 
@@ -46,12 +46,16 @@ def flags():
     ]
 
 
-# Extra flags per source.  The dQ kernel (attn_bwd.hip) is scheduled with the
-# compiler's max-ILP strategy: measured at CAUSAL 32K GQA 64:8, dQ 21.43 ->
-# 21.20 ms (three alternating runs on one box); the same strategy gave the
-# forward nothing and changed the dK/dV file's D = 256 register allocation.
+# Extra flags per source, each measured at CAUSAL 32K GQA 64:8 over
+# alternating runs on one box.  The dQ kernel (attn_bwd.hip) is scheduled with
+# the compiler's max-ILP strategy (dQ 21.43 -> 21.20 ms), the head-dim 64 /
+# 128 dK/dV instances (attn_dkdv.hip) with iterative ILP scheduling (dK/dV
+# 33.81 -> 33.48 ms); the head-dim 256 instances are built from a file of
+# their own without it, as it changes their register allocation.  The forward
+# gained nothing from either.
 SOURCE_FLAGS = {
     "attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "attn_dkdv.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
 }
 
 
