@@ -27,8 +27,9 @@ def spec_kwargs(spec):
     return kw
 
 
-def gpu_attention(plan, q, k, v, do, scale, bwd=True, o_in=None, lse_in=None):
-    """Run fwd (and bwd) on cuda:0.  q, k, v, do are CPU bf16 tensors.  Returns CPU float64 arrays."""
+def gpu_attention(plan, q, k, v, do, scale, bwd=True, o_in=None, lse_in=None, fill=None):
+    """Run fwd (and bwd) on cuda:0.  q, k, v, do are CPU bf16 tensors.  Returns CPU float64 arrays.
+    fill: a value the output buffers hold before the calls (default: whatever torch.empty gives)."""
     import mask_aware_dense_amd as mad
     torch = torch_mod()
     dev = torch.device("cuda", 0)
@@ -36,17 +37,20 @@ def gpu_attention(plan, q, k, v, do, scale, bwd=True, o_in=None, lse_in=None):
     Tq, Hq, d = q.shape
     Tk, Hkv, _ = k.shape
     plan.upload()
-    o = torch.empty((Tq, Hq, d), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((Hq, Tq), dtype=torch.float32, device=dev)
+    def out_like(shape, dtype):
+        t = torch.empty(shape, dtype=dtype, device=dev)
+        return t if fill is None else t.fill_(fill)
+    o = out_like((Tq, Hq, d), torch.bfloat16)
+    lse = out_like((Hq, Tq), torch.float32)
     mad.attn_fwd(plan, qd, kd, vd, o, lse, scale)
     out = {}
     if bwd:
         dod = do.to(dev)
         oi = o if o_in is None else o_in.to(dev)
         li = lse if lse_in is None else lse_in.to(dev)
-        dq = torch.empty_like(qd)
-        dk = torch.empty_like(kd)
-        dv = torch.empty_like(vd)
+        dq = out_like(tuple(qd.shape), torch.bfloat16)
+        dk = out_like(tuple(kd.shape), torch.bfloat16)
+        dv = out_like(tuple(vd.shape), torch.bfloat16)
         ws = torch.empty(max(mad.bwd_workspace_bytes(plan, Tq, Tk, Hq, Hkv, d), 256), dtype=torch.uint8, device=dev)
         mad.attn_bwd(plan, qd, kd, vd, oi, dod, li, dq, dk, dv, ws, scale)
         out.update(dq=dq, dk=dk, dv=dv)

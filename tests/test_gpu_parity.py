@@ -146,6 +146,39 @@ def test_empty_key_range_gives_zero_and_neg_inf():
     assert np.all(got["o"] == 0) and np.all(np.isneginf(got["lse"])) and np.all(got["dq"] == 0)
 
 
+@pytest.mark.parametrize("Tq,Tk,slices", [
+    # keys 200..329 are seen by no row (a gap between a full and a causal slice)
+    (300, 500, ((0, 300, 0, 200, 0, 0), (0, 300, 330, 500, 1, 0))),
+    # no query rows at all: every key's dK, dV is 0
+    (0, 300, ()),
+])
+def test_unseen_keys_get_zero_gradients(Tq, Tk, slices):
+    """dK = dV = 0 are written for keys no query row sees, whatever the output buffers held
+    before the calls (NaN here); the other outputs match the oracle."""
+    import mask_aware_dense_amd as mad
+    spec = M.MaskSpec("SLICES", Tq, Tk, slices=tuple(slices))
+    arr = np.array(list(slices), dtype=mad.SLICE_DTYPE) if slices else np.zeros(0, dtype=mad.SLICE_DTYPE)
+    plan = mad.mask_compile(arr, Tq, Tk)
+    Hq, Hkv, d = 4, 2, 128
+    q, k, v = qkv(11, Tq, Tk, Hq, Hkv, d)
+    do = grad_out(11, Tq, Hq, d)
+    scale = 1.0 / np.sqrt(d)
+    print(f"case unseen keys Tq={Tq} Tk={Tk}", flush=True)
+    got = _gpu.gpu_attention(plan, q, k, v, do, scale, fill=float("nan"))
+    g = A.attn_bwd(q, k, v, do, spec, scale)
+    seen = np.zeros(Tk, dtype=bool)
+    for (q0, q1, k0, k1, _t, _w) in slices:
+        seen[k0:k1] = q1 > q0
+    assert np.all(got["dk"][~seen] == 0) and np.all(got["dv"][~seen] == 0)
+    for n in ("dk", "dv"):
+        _gpu.check_close(n, got[n], g[n], _gpu.TOL_BWD)
+    if Tq:
+        O, L = A.attn_fwd(q, k, v, spec, scale)
+        _gpu.check_close("o", got["o"], O, _gpu.TOL_FWD)
+        _gpu.check_lse(got["lse"], L)
+        _gpu.check_close("dq", got["dq"], g["dq"], _gpu.TOL_BWD)
+
+
 def test_rectangular_slices():
     """Tq != Tk with an arbitrary overlapping slice union."""
     import mask_aware_dense_amd as mad
