@@ -27,9 +27,10 @@ def spec_kwargs(spec):
     return kw
 
 
-def gpu_attention(plan, q, k, v, do, scale, bwd=True, o_in=None, lse_in=None, fill=None):
+def gpu_attention(plan, q, k, v, do, scale, bwd=True, o_in=None, lse_in=None, fill=float("nan")):
     """Run fwd (and bwd) on cuda:0.  q, k, v, do are CPU bf16 tensors.  Returns CPU float64 arrays.
-    fill: a value the output buffers hold before the calls (default: whatever torch.empty gives)."""
+    fill: the value the output buffers hold before the calls (NaN, so that an element the kernels
+    leave unwritten fails the comparison; None leaves torch.empty's contents)."""
     import mask_aware_dense_amd as mad
     torch = torch_mod()
     dev = torch.device("cuda", 0)
