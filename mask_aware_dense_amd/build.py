@@ -35,9 +35,8 @@ def flags():
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", os.path.join(ROOT, "include"), "-Wno-unused-result",
         # MFMA results in arch VGPRs: the score tiles feed VALU softmax code
-        # directly, and the register allocator then keeps the kernels
-        # spill-free but for the one listed in VALIDATED_SCRATCH (measured:
-        # forward 58.9 -> 22.7 ms at 32K causal)
+        # directly, and the register allocator then keeps every kernel
+        # spill-free (measured: forward 58.9 -> 22.7 ms at 32K causal)
         "-mllvm", "-amdgpu-mfma-vgpr-form",
         # the D = 256 step loops are longer than the default full-unroll
         # budget; partly unrolled, their operand arrays would be indexed at
@@ -50,9 +49,9 @@ def flags():
 # alternating runs on one box.  The dQ kernel (attn_bwd.hip) is scheduled with
 # the compiler's max-ILP strategy (dQ 21.43 -> 21.20 ms), the head-dim 64 /
 # 128 dK/dV instances (attn_dkdv.hip) with iterative ILP scheduling (dK/dV
-# 33.81 -> 33.48 ms); the head-dim 256 instances are built from a file of
-# their own without it, as it changes their register allocation.  The forward
-# gained nothing from either.
+# 33.81 -> 33.48 ms).  The forward and the head-dim 256 dK/dV kernel
+# (attn_dkdv256.hip, timed at CAUSAL 32K GQA 64:8 d=256) gained nothing from
+# either.
 SOURCE_FLAGS = {
     "attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
     "attn_dkdv.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
@@ -64,12 +63,8 @@ SOURCE_FLAGS = {
 # stores to the vector-memory counter that the direct global->LDS copies are
 # waited on with, so a changed register allocation must not slip in
 # unnoticed: the build fails when any kernel's scratch size differs from its
-# recorded value (0 for every kernel not listed).
-VALIDATED_SCRATCH = {
-    # head dim 256, 64-key tiles in two-wave workgroups: 7 registers spilled
-    "_ZN3mad11dkdv_kernelILi256ELi2ELb0EEEvNS_10AttnParamsE": 24,
-    "_ZN3mad11dkdv_kernelILi256ELi2ELb1EEEvNS_10AttnParamsE": 24,
-}
+# recorded value (0 for every kernel not listed; none spills now).
+VALIDATED_SCRATCH: dict = {}
 
 
 def _scratch_sizes(stderr: str) -> dict:

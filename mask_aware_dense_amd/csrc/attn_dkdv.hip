@@ -23,21 +23,20 @@ __global__ __launch_bounds__(256) void round2_kernel(const float* a, const float
   }
 }
 
-// Head dim 256 launches from its own source file (attn_dkdv256.hip), which
-// is compiled without this file's scheduling flag.
-hipError_t launch_dkdv_d256(const AttnParams& P, dim3 grid, bool fine, bool hm, hipStream_t stream);
+// Head dim 256 has a kernel of its own (attn_dkdv256.hip).
+hipError_t launch_dkdv_d256(const AttnParams& P, int n_items, bool hm, hipStream_t stream);
 
 hipError_t launch_dkdv(const AttnParams& P, int D, int n_items, hipStream_t stream) {
   const int S = P.kv_splits;
   const int64_t n4 = (int64_t)P.Tk * P.Hkv * D / 4;  // D is a multiple of 4
   const int nb = (int)std::min<int64_t>((n4 + 255) / 256, 4096);
   if (S > 1 && n4 > 0) hipLaunchKernelGGL(zero2_kernel, dim3(nb), dim3(256), 0, stream, P.dk_acc, P.dv_acc, n4);
-  const dim3 grid(n_items * S, D == 256 ? 2 : 1);
+  const dim3 grid(n_items * S);
   auto run = [&](auto k, int nw) { hipLaunchKernelGGL(k, grid, dim3(64 * nw), 0, stream, P); };
   const bool hm = P.R == 1 && (P.m.mode == MODE_BLOCKS || P.t.uniform);
   const bool fine = P.t.BN == BN1_FINE;
   if (D == 256) {
-    const hipError_t e = launch_dkdv_d256(P, grid, fine, hm, stream);
+    const hipError_t e = launch_dkdv_d256(P, n_items, hm, stream);
     if (e != hipSuccess) return e;
   } else if (D == 128) {
     if (fine) hm ? run(dkdv_kernel<128, 2, true>, 2) : run(dkdv_kernel<128, 2, false>, 2);

@@ -1,5 +1,5 @@
-// attn_dkdv.hpp -- dK / dV kernel for gfx950 (device code, included by
-// attn_dkdv.hip for head dims 64 and 128 and by attn_dkdv256.hip for 256).
+// attn_dkdv.hpp -- dK / dV kernel for gfx950, head dims 64 and 128 (device
+// code, included by attn_dkdv.hip; attn_dkdv256.hip shares its item walk).
 //
 // For every key j of a KV head and every query head h of its GQA group
 // (LongCA-bench section 3.2 names the backward pass as the bottleneck):
@@ -135,27 +135,21 @@ struct KvWalk {
   }
 };
 
-// At D = 256 each workgroup accumulates one 128-column half of dK / dV
-// (blockIdx.y), with S and dP still taken over all of D: K, V and both full
-// accumulators would not fit in a lane's 512 registers.
 // NW waves of 32 keys: a 128-key tile (NW = 4, one workgroup per CU) or,
 // for block-sparse plans of 64-token key blocks, a 64-key tile (NW = 2, two
 // workgroups per CU).
 // HM: the head-major item order (MHA masks whose columns carry even work).
 template <int D, int NW, bool HM>
 __global__ __launch_bounds__(64 * NW) void dkdv_kernel(const AttnParams P) {
-  constexpr int DO = D == 256 ? 128 : D;  // dK / dV columns per workgroup
-  constexpr int BM = BM1, BN = 32 * NW, NKS = D / 16, NDB = DO / 32;
-  const int c0 = D == 256 ? (int)blockIdx.y * DO : 0;  // first dK / dV column
+  static_assert(D == 64 || D == 128, "head dim 256 has a kernel of its own");
+  constexpr int BM = BM1, BN = 32 * NW, NKS = D / 16, NDB = D / 32;
   // D = 128: unpadded swizzled Q / dO tiles; D = 64: padded rows.
   constexpr int KIND = D == 128 ? TILE_SWZ : TILE_MIXED;
   constexpr int TILE = tile_elems<D, KIND>(), RS = tile_rs<D, KIND>();
   constexpr int S1 = 2 * NKS;   // phase-1 steps (block, k-step)
   constexpr int S2 = 4 * NDB;   // phase-2 steps (block, t2, d-block)
-  // LDS operands are read RA steps ahead through rings of RA + 1 slots (one
-  // step at D = 256, where two would not leave registers to spare, and none
-  // for the two-wave D = 256 form).
-  constexpr int RA = D == 256 ? (NW == 2 ? 0 : 1) : 2, NR = RA + 1;
+  // LDS operands are read RA steps ahead through rings of RA + 1 slots.
+  constexpr int RA = 2, NR = RA + 1;
   constexpr int EB = 16 / NKS >= 2 ? 16 / NKS : 2;  // P / dS elements per stage-B step (the first 16 / EB steps)
   constexpr int EC = 16 / (2 * NDB);  // P / dS elements per stage-C step
   __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];   // Q0 dO0 Q1 dO1
@@ -308,7 +302,7 @@ __global__ __launch_bounds__(64 * NW) void dkdv_kernel(const AttnParams P) {
           trd[st % NR] = ld_tr8((const bf16*)(dc + rb + str.o0[db]), (const bf16*)(dc + rb + str.o1[db]));
           trq[st % NR] = ld_tr8((const bf16*)(qc + rb + str.o0[db]), (const bf16*)(qc + rb + str.o1[db]));
         } else {
-          const int qrow = b * 32 + 16 * t2 + 4 * hh + tr_row(lane), col = c0 + db * 32 + tr_col(lane);
+          const int qrow = b * 32 + 16 * t2 + 4 * hh + tr_row(lane), col = db * 32 + tr_col(lane);
           trd[st % NR] = ld_tr8(Ds + qrow * RS + col, Ds + (qrow + 8) * RS + col);
           trq[st % NR] = ld_tr8(Qs + qrow * RS + col, Qs + (qrow + 8) * RS + col);
         }
@@ -377,7 +371,7 @@ __global__ __launch_bounds__(64 * NW) void dkdv_kernel(const AttnParams P) {
         for (int r = 0; r < 16; ++r) {
           const int kk = kt * BN + w * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
           if (kk < P.Tk) {
-            const int64_t off = ((int64_t)kk * P.Hkv + g) * D + c0 + db * 32 + li;
+            const int64_t off = ((int64_t)kk * P.Hkv + g) * D + db * 32 + li;
             unsafeAtomicAdd(P.dk_acc + off, dka[db][r] * P.scale);
             unsafeAtomicAdd(P.dv_acc + off, dva[db][r]);
           }
@@ -391,7 +385,7 @@ __global__ __launch_bounds__(64 * NW) void dkdv_kernel(const AttnParams P) {
     for (int r = 0; r < 16; ++r) {
       const int kk = kt * BN + w * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
       if (kk < P.Tk) {
-        const int64_t off = ((int64_t)kk * P.Hkv + g) * D + c0 + db * 32 + li;
+        const int64_t off = ((int64_t)kk * P.Hkv + g) * D + db * 32 + li;
         P.dk[off] = (bf16)(dka[db][r] * P.scale);
         P.dv[off] = (bf16)dva[db][r];
       }
