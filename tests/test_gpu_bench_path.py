@@ -51,20 +51,21 @@ def test_causal_16k_gqa_16_8():
 
 @pytest.mark.parametrize("d", [128, 256])
 def test_causal_4k_gqa_64_32(d):
-    """CAUSAL 4K, GQA 64:32 (two query heads per KV head) at head dims 128 and 256 (the latter in two
-    column halves per key tile): every head checked."""
+    """CAUSAL 4K, GQA 64:32 (two query heads per KV head) at head dims 128 and 256 (the latter through
+    the pair-of-waves dK/dV kernel, two 64-key workgroups per 128-key tile): every head checked."""
     import mask_aware_dense_amd as mad
     T = 4096
     plan = mad.mask_compile(mad.mask_slices("CAUSAL", T), T, T)
     _run_and_check(plan, M.MaskSpec("CAUSAL", T, T), 64, 32, d, seed=22, heads=range(64))
 
 
-def test_full_4k_mha_16():
+@pytest.mark.parametrize("d", [128, 256])
+def test_full_4k_mha_16(d):
     """FULL 4K MHA 16:16: every visit list has one length, so the head-major kernels run."""
     import mask_aware_dense_amd as mad
     T = 4096
     plan = mad.mask_compile(mad.mask_slices("FULL", T), T, T)
-    _run_and_check(plan, M.MaskSpec("FULL", T, T), 16, 16, 128, seed=23, heads=range(16), bn=128)
+    _run_and_check(plan, M.MaskSpec("FULL", T, T), 16, 16, d, seed=23, heads=range(16), bn=128)
 
 
 def _sparse(T, b, G, pct, seed):
@@ -77,10 +78,12 @@ def _sparse(T, b, G, pct, seed):
     return plan, spec
 
 
-def test_block_sparse_mha_8_b64_s80_8k():
-    """Block-sparse MHA 8:8, 64-token blocks, 80% dropped: head-major 64-key two-wave dK/dV tiles."""
+@pytest.mark.parametrize("d", [128, 256])
+def test_block_sparse_mha_8_b64_s80_8k(d):
+    """Block-sparse MHA 8:8, 64-token blocks, 80% dropped: head-major 64-key dK/dV tiles (two-wave
+    workgroups at d = 128, one pair-of-waves workgroup per tile at d = 256)."""
     plan, spec = _sparse(8192, 64, 8, 80, seed=24)
-    _run_and_check(plan, spec, 8, 8, 128, seed=24, heads=range(8), bn=64)
+    _run_and_check(plan, spec, 8, 8, d, seed=24, heads=range(8), bn=64)
 
 
 def test_block_sparse_gqa_16_8_b128_s50_16k():

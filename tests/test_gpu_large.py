@@ -62,7 +62,8 @@ def test_causal_32k_gqa_64_8():
 
 
 def test_causal_16k_gqa_64_8_d256():
-    """Head dim 256 at a full size: CAUSAL, T=16384, GQA 64:8 (dQ, dK, dV in two column halves)."""
+    """Head dim 256 at a full size: CAUSAL, T=16384, GQA 64:8 (dK, dV from pairs of waves that each
+    keep one column half)."""
     spec = M.MaskSpec("CAUSAL", 16384, 16384)
     q, k, v, do, scale, got = _full_run(spec, 64, 8, 256, seed=4)
     _check_sampled(spec, q, k, v, do, scale, got, n_rows=24, heads=[0, 9, 40, 63])

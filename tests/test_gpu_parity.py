@@ -101,7 +101,8 @@ def test_block_sparse(b, variable, pct, heads):
 @pytest.mark.parametrize("b,variable", [(64, False), (0, True)])
 @pytest.mark.parametrize("heads", [(8, 8), (8, 2)], ids=["mha", "gqa"])
 def test_block_sparse_d256(b, variable, heads):
-    """Head dim 256 (dQ, dK and dV in two 128-column halves) under mixed-strip block masks."""
+    """Head dim 256 (dK and dV from pairs of waves that each keep one 128-column half) under
+    mixed-strip block masks."""
     Hq, Hkv = heads
     T = 1536 if not variable else 1333
     plan, spec = _sparse(T, b, Hkv, 50, seed=b + Hkv + 256, variable=variable)
