@@ -313,7 +313,11 @@ mad_status mad_attn_fwd(const mad_plan* plan, const void* q, const void* k, cons
  * (-inf for rows with no allowed key and for padding rows), and, when the
  * plan's key-tile columns are uneven enough that the dK/dV kernel cuts the
  * longest ones between several workgroups (mad_bwd_kv_splits > 1), two fp32
- * [Tk][Hkv][d] sums for dK and dV.  Depends on the plan and on the compute
+ * [Tk][Hkv][d] sums for dK and dV; last, 256 bytes of counters through
+ * which the dQ kernel's workgroups claim their work items (the XCDs run at
+ * different speeds, and the faster ones take over the slower ones' last
+ * items; the counters are cleared on the stream before each use).  Depends
+ * on the plan and on the compute
  * units of the current device, so query it per plan.  Host only; launches
  * nothing.  Errors: MAD_ERR_INVALID for NULL arguments or bad sizes,
  * MAD_ERR_UNSUPPORTED for a head dim other than 64 / 128 / 256. */

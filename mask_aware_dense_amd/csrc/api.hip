@@ -22,7 +22,7 @@ mad_status fail(mad_status s, const std::string& msg) {
 void clear_error() { g_err.clear(); }
 
 hipError_t launch_fwd(const AttnParams& P, int D, int n_items, hipStream_t stream);
-hipError_t launch_bwd(const AttnParams& Pq, const AttnParams& Pkv, int D, int nq_items, int nkv_items,
+hipError_t launch_bwd(AttnParams Pq, const AttnParams& Pkv, int D, int nq_items, int nkv_items,
                       uint32_t phases, hipStream_t stream);
 
 namespace {
@@ -86,6 +86,9 @@ int device_cus() {
   }
   return n;
 }
+
+// Workspace bytes of the dQ kernel's item-claim counters (8 used).
+constexpr size_t kQueueBytes = 256;
 
 // Workgroups per key-tile column of the dK/dV kernel.  The kernel runs one
 // workgroup per CU; when its longest column holds more than half of one CU's
@@ -287,10 +290,12 @@ extern "C" mad_status mad_bwd_workspace_bytes(const mad_plan* p, int32_t Tq, int
   if (d != 64 && d != 128 && d != 256)
     return fail(MAD_ERR_UNSUPPORTED, "mad_bwd_workspace_bytes: head dim must be 64, 128 or 256");
   // -delta and -LSE/scale rows, each [Hq][Tq rounded up to 128] fp32; with
-  // split dK/dV columns, fp32 dK and dV sums [Tk][Hkv][d] after them
+  // split dK/dV columns, fp32 dK and dV sums [Tk][Hkv][d] after them; last,
+  // 256 bytes for the dQ kernel's item-claim counters
   const size_t tq_pad = ((size_t)Tq + 127) / 128 * 128;
   *bytes = (2 * (size_t)Hq * tq_pad * 4 + 255) / 256 * 256;
   if (Hq % Hkv == 0 && Hq % p->G == 0 && dkdv_splits(p, Hq, Hkv) > 1) *bytes += 2 * (size_t)Tk * Hkv * d * 4;
+  *bytes += kQueueBytes;
   return MAD_OK;
 }
 
@@ -347,6 +352,8 @@ mad_status attn_bwd_impl(const mad_plan* p, const void* q, const void* k, const 
     Pkv.dv_acc = (float*)acc + (size_t)Tk * Hkv * d;
   }
   Pq.kv_splits = 1;
+  // the dQ kernel's item-claim counters: the last kQueueBytes of the workspace
+  Pq.queue = Tq > 0 ? (int32_t*)((char*)workspace + need - kQueueBytes) : nullptr;
   const int64_t nq = Tq > 0 ? (int64_t)p->tiling[0].nqt * Hq : 0;
   const int64_t nkv = Tk > 0 ? (int64_t)p->tiling[1].nkt * Hkv : 0;
   if (nq > INT32_MAX || nkv > INT32_MAX) return fail(MAD_ERR_UNSUPPORTED, "mad_attn_bwd: too many work items");

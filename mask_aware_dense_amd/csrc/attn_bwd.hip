@@ -96,7 +96,14 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void dq_kernel(const AttnPar
   // forward fetched 95 GB at 32K, b = 64, s = 0.8).  Masks with uneven tiles
   // keep ranks outermost, where the longest-first order balances the CUs.
   constexpr bool mha = HM;  // launched only for P.R == 1
-  const int L = mha ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
+  // The item is claimed from the per-XCD queues (claim_item); the grid holds
+  // more workgroups than items, and those that find every queue empty exit.
+  __shared__ int claimed;
+  if (threadIdx.x == 0) claimed = claim_item(P.queue, P.n_items);
+  __syncthreads();
+  const int item = __builtin_amdgcn_readfirstlane(claimed);  // uniform: in scalar registers
+  if (item < 0) return;
+  const int L = mha ? item : xcd_remap(item, P.n_items);
   const int e = mha ? 0 : L % P.R, t_ = mha ? L : L / P.R;
   const int g = mha ? t_ / P.t.nmajor : t_ % P.Hkv, rank = mha ? t_ % P.t.nmajor : t_ / P.Hkv;
   const int h = g * P.R + e;
@@ -274,7 +281,13 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void dq_kernel(const AttnPar
 
 hipError_t launch_dkdv(const AttnParams& P, int D, int n_items, hipStream_t stream);
 
-hipError_t launch_bwd(const AttnParams& Pq, const AttnParams& Pkv, int D, int nq_items, int nkv_items,
+// The dQ kernel's 8 item-claim counters start at zero (a kernel rather than
+// a memset, so that the backward can be captured in a graph).
+__global__ __launch_bounds__(64) void queue_reset_kernel(int32_t* q) {
+  if (threadIdx.x < 8) q[threadIdx.x] = 0;
+}
+
+hipError_t launch_bwd(AttnParams Pq, const AttnParams& Pkv, int D, int nq_items, int nkv_items,
                       uint32_t phases, hipStream_t stream) {
   const int64_t nrows = (int64_t)Pq.Tq_pad * Pq.Hq;
   if ((phases & MAD_BWD_DELTA) && nrows > 0) {
@@ -284,14 +297,17 @@ hipError_t launch_bwd(const AttnParams& Pq, const AttnParams& Pkv, int D, int nq
     else if (D == 256) hipLaunchKernelGGL(delta_kernel<256>, dim3(nb), dim3(256), 0, stream, Pq);
     else hipLaunchKernelGGL(delta_kernel<64>, dim3(nb), dim3(256), 0, stream, Pq);
   }
+  const bool kv = (phases & MAD_BWD_DKDV) && nkv_items > 0, dq = (phases & MAD_BWD_DQ) && nq_items > 0;
+  if (dq) hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(64), 0, stream, Pq.queue);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if ((phases & MAD_BWD_DKDV) && nkv_items > 0) {
+  if (kv) {
     err = launch_dkdv(Pkv, D, nkv_items, stream);
     if (err != hipSuccess) return err;
   }
-  if ((phases & MAD_BWD_DQ) && nq_items > 0) {
-    auto run = [&](auto k) { hipLaunchKernelGGL(k, dim3(nq_items), dim3(256), 0, stream, Pq); };
+  if (dq) {
+    Pq.n_items = nq_items;
+    auto run = [&](auto k) { hipLaunchKernelGGL(k, dim3(claim_grid(nq_items)), dim3(256), 0, stream, Pq); };
     if (Pq.R == 1 && (Pq.m.mode == MODE_BLOCKS || Pq.t.uniform)) {
       if (D == 128) run(dq_kernel<128, true>);
       else if (D == 256) run(dq_kernel<256, true>);

@@ -19,7 +19,8 @@ def _run_and_check(plan, spec, Hq, Hkv, d, seed, heads, bn=None):
     import mask_aware_dense_amd as mad
     T = spec.Tq
     assert mad.bwd_kv_splits(plan, Hq, Hkv) == 1
-    ws_one = (2 * Hq * ((T + 127) // 128 * 128) * 4 + 255) // 256 * 256
+    # -delta and -LSE/scale rows, then the kernels' 256 bytes of item-claim counters
+    ws_one = (2 * Hq * ((T + 127) // 128 * 128) * 4 + 255) // 256 * 256 + 256
     assert mad.bwd_workspace_bytes(plan, T, T, Hq, Hkv, d) == ws_one  # no fp32 dK / dV sums
     if bn is not None:
         assert plan.info(1)["BN"] == bn
