@@ -211,6 +211,7 @@ class Runner:
         self.lse = torch.empty((Hq, Tq), dtype=torch.float32, device=dev)
         self.dq, self.dk, self.dv = torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v)
         self.ws = torch.empty(mad.bwd_workspace_bytes(plan, Tq, Tk, Hq, Hkv, d), dtype=torch.uint8, device=dev)
+        self.fws = torch.empty(mad.FWD_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
         self.scale = 1.0 / np.sqrt(d)
         self.stream = torch.cuda.current_stream()
 
@@ -225,7 +226,7 @@ class Runner:
         mad, s = self.mad, self.stream
         if evs is not None:
             evs[0].record(s)
-        mad.attn_fwd(self.plan, self.q, self.k, self.v, self.o, self.lse, self.scale, s)
+        mad.attn_fwd(self.plan, self.q, self.k, self.v, self.o, self.lse, self.scale, s, workspace=self.fws)
         if evs is not None:
             evs[1].record(s)
         if fwd_only:
@@ -633,15 +634,16 @@ def peak_memory_case(torch, mad, mask, T, Hq, Hkv, d, seed, kw=None):
     q, k, v = (x.to(dev) for x in qkv(seed, T, T, Hq, Hkv, d))
     o = torch.empty_like(q)
     lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    fws = torch.empty(mad.FWD_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
     scale = 1.0 / np.sqrt(d)
     torch.cuda.synchronize()
     live_f = torch.cuda.memory_allocated() - base  # the forward's tensors as the allocator counts them
     free0 = torch.cuda.mem_get_info()[0]
-    mad.attn_fwd(plan, q, k, v, o, lse, scale)
+    mad.attn_fwd(plan, q, k, v, o, lse, scale, workspace=fws)
     torch.cuda.synchronize()
     free_f = torch.cuda.mem_get_info()[0]
     fwd_peak = torch.cuda.max_memory_allocated() - base + pb
-    fwd_sum = sum(_alloc_bytes(t) for t in (q, k, v, o, lse)) + pb
+    fwd_sum = sum(_alloc_bytes(t) for t in (q, k, v, o, lse, fws)) + pb
     do = grad_out(seed, T, Hq, d).to(dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(mad.bwd_workspace_bytes(plan, T, T, Hq, Hkv, d), dtype=torch.uint8, device=dev)
@@ -659,7 +661,7 @@ def peak_memory_case(torch, mad, mask, T, Hq, Hkv, d, seed, kw=None):
            "free_bytes_change_fwd": int(free0) - int(free_f),
            "free_bytes_change_bwd": int(free1) - int(free2),
            "standard_attention_activation_model_bytes": activation_model_bytes(1, T, Hq, d)}
-    del q, k, v, o, lse, do, dq, dk, dv, ws, plan
+    del q, k, v, o, lse, fws, do, dq, dk, dv, ws, plan
     return rec
 
 

@@ -298,12 +298,31 @@ void mad_plan_destroy(mad_plan* plan);
  * been compiled for (Tq, Tk), uploaded, and have n_groups dividing Hq.
  * ------------------------------------------------------------------------- */
 
+/* Device workspace of mad_attn_fwd (optional): 8 counters through which
+ * the kernel's workgroups claim their work items. */
+#define MAD_FWD_WORKSPACE_BYTES 256
+
 /* Forward: O = softmax(scale * Q K^T + mask) V and LSE (LongCA-bench
  * section 1: standard softmax attention).  Tiled with an online softmax;
- * only non-EMPTY tiles are visited and only PARTIAL tiles evaluate the mask. */
+ * only non-EMPTY tiles are visited and only PARTIAL tiles evaluate the mask.
+ *   q, k, v: device bf16, [Tq, Hq, d] and [Tk, Hkv, d] with the strides
+ *     above; o: device bf16 [Tq, Hq, d] packed; lse: device fp32 [Hq, Tq]
+ *     (natural log; -inf, with O = 0, for rows that see no key).
+ *   workspace: NULL, or device memory of at least MAD_FWD_WORKSPACE_BYTES,
+ *     256-byte aligned, owned by the caller, contents on entry irrelevant.
+ *     With it, workgroups claim work items from per-XCD queues and the
+ *     faster XCDs take over the slower ones' last items (the XCDs run at
+ *     different speeds); without it each workgroup takes a fixed item.  The
+ *     result is the same either way.  Calls that may overlap on the GPU
+ *     (other streams) must not share a workspace.
+ * Errors: MAD_ERR_INVALID for a NULL plan, mismatched shapes, NULL o / lse
+ * (Tq > 0), a NaN scale or a short workspace; MAD_ERR_UNSUPPORTED for
+ * misaligned pointers or strides or an unsupported head dim; MAD_ERR_HIP for
+ * a failed launch. */
 mad_status mad_attn_fwd(const mad_plan* plan, const void* q, const void* k, const void* v,
                         void* o, float* lse, int32_t Tq, int32_t Tk, int32_t Hq, int32_t Hkv,
-                        int32_t d, const int64_t* strides, float scale, hipStream_t stream);
+                        int32_t d, const int64_t* strides, float scale, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of device workspace mad_attn_bwd needs (LongCA-bench section 3.2:
  * the backward is the harder pass and only some kernels have one; appendix

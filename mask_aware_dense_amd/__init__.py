@@ -75,7 +75,8 @@ _SIGS = {
     "mad_plan_export": (_I32, [_VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP]),
     "mad_plan_destroy": (None, [_VP]),
     "mad_plan_device_bytes": (_I32, [_VP, ctypes.POINTER(ctypes.c_size_t)]),
-    "mad_attn_fwd": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP, _F32, _VP]),
+    "mad_attn_fwd": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP, _F32, _VP,
+                            ctypes.c_size_t, _VP]),
     "mad_bwd_workspace_bytes": (_I32, [_VP, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)]),
     "mad_bwd_kv_splits": (_I32, [_VP, _I32, _I32, _PI32]),
     "mad_attn_bwd": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
@@ -350,14 +351,20 @@ def _check_workspace(workspace):
     return workspace.numel() * workspace.element_size()
 
 
-def attn_fwd(plan: Plan, q, k, v, o, lse, scale: float, stream=None):
-    """Forward into preallocated o [Tq,Hq,d] bf16 and lse [Hq,Tq] fp32 (torch CUDA tensors)."""
+FWD_WORKSPACE_BYTES = 256
+
+
+def attn_fwd(plan: Plan, q, k, v, o, lse, scale: float, stream=None, workspace=None):
+    """Forward into preallocated o [Tq,Hq,d] bf16 and lse [Hq,Tq] fp32 (torch CUDA tensors).  workspace:
+    None, or a device buffer of at least FWD_WORKSPACE_BYTES (its work-item counters; not shared by calls
+    that may run at the same time)."""
     Tq, Hq, d = q.shape
     Tk, Hkv, _ = k.shape
     _check_tensors(q, k, v, {"o": (o, (Tq, Hq, d))}, lse)
     st = _qkv_strides(q, k, v)
+    nbytes = _check_workspace(workspace)
     _check(lib().mad_attn_fwd(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), Tq, Tk, Hq, Hkv, d,
-                              st, float(scale), _stream(stream)))
+                              st, float(scale), _ptr(workspace), nbytes, _stream(stream)))
 
 
 def bwd_workspace_bytes(plan: Plan, Tq: int, Tk: int, Hq: int, Hkv: int, d: int) -> int:

@@ -21,7 +21,7 @@ mad_status fail(mad_status s, const std::string& msg) {
 }
 void clear_error() { g_err.clear(); }
 
-hipError_t launch_fwd(const AttnParams& P, int D, int n_items, hipStream_t stream);
+hipError_t launch_fwd(AttnParams P, int D, int n_items, hipStream_t stream);
 hipError_t launch_bwd(AttnParams Pq, const AttnParams& Pkv, int D, int nq_items, int nkv_items,
                       uint32_t phases, hipStream_t stream);
 
@@ -262,7 +262,7 @@ extern "C" void mad_plan_destroy(mad_plan* p) {
 
 extern "C" mad_status mad_attn_fwd(const mad_plan* p, const void* q, const void* k, const void* v, void* o, float* lse,
                                    int32_t Tq, int32_t Tk, int32_t Hq, int32_t Hkv, int32_t d, const int64_t* strides,
-                                   float scale, hipStream_t stream) {
+                                   float scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   clear_error();
   Strides st;
   mad_status s = check_common("mad_attn_fwd", p, q, k, v, Tq, Tk, Hq, Hkv, d, strides, st);
@@ -270,10 +270,14 @@ extern "C" mad_status mad_attn_fwd(const mad_plan* p, const void* q, const void*
   if (Tq > 0 && (!o || !lse)) return fail(MAD_ERR_INVALID, "mad_attn_fwd: o/lse must not be NULL");
   if (!aligned16(o) || ((uintptr_t)lse & 3u)) return fail(MAD_ERR_UNSUPPORTED, "mad_attn_fwd: o must be 16-byte and lse 4-byte aligned");
   if (!(scale == scale)) return fail(MAD_ERR_INVALID, "mad_attn_fwd: scale is NaN");
+  if (workspace && workspace_bytes < MAD_FWD_WORKSPACE_BYTES)
+    return fail(MAD_ERR_INVALID, "mad_attn_fwd: workspace must hold " + std::to_string(MAD_FWD_WORKSPACE_BYTES) + " bytes");
+  if ((uintptr_t)workspace & 255u) return fail(MAD_ERR_UNSUPPORTED, "mad_attn_fwd: workspace must be 256-byte aligned");
   if (Tq == 0) return MAD_OK;
   AttnParams P = base_params(p, 0, q, k, v, Tq, Tk, Hq, Hkv, st, scale);
   P.o = (bf16*)o;
   P.lse = lse;
+  P.queue = (int32_t*)workspace;  // item-claim counters, or NULL: one fixed item per workgroup
   const int64_t n_items = (int64_t)p->tiling[0].nqt * Hq;
   if (n_items > INT32_MAX) return fail(MAD_ERR_UNSUPPORTED, "mad_attn_fwd: too many work items");
   hipError_t e = launch_fwd(P, d, (int)n_items, stream);

@@ -281,12 +281,6 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void dq_kernel(const AttnPar
 
 hipError_t launch_dkdv(const AttnParams& P, int D, int n_items, hipStream_t stream);
 
-// The dQ kernel's 8 item-claim counters start at zero (a kernel rather than
-// a memset, so that the backward can be captured in a graph).
-__global__ __launch_bounds__(64) void queue_reset_kernel(int32_t* q) {
-  if (threadIdx.x < 8) q[threadIdx.x] = 0;
-}
-
 hipError_t launch_bwd(AttnParams Pq, const AttnParams& Pkv, int D, int nq_items, int nkv_items,
                       uint32_t phases, hipStream_t stream) {
   const int64_t nrows = (int64_t)Pq.Tq_pad * Pq.Hq;

@@ -58,7 +58,15 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
   // forward fetched 95 GB at 32K, b = 64, s = 0.8).  Masks with uneven tiles
   // keep ranks outermost, where the longest-first order balances the CUs.
   constexpr bool mha = HM;  // launched only for P.R == 1
-  const int L = mha ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
+  // With a workspace the item is claimed from the per-XCD queues (claim_item;
+  // the grid holds more workgroups than items, and those that find every
+  // queue empty exit); without one, workgroup b takes item b.
+  __shared__ int claimed;
+  if (threadIdx.x == 0) claimed = P.queue ? claim_item(P.queue, P.n_items) : (int)blockIdx.x;
+  __syncthreads();
+  const int item = __builtin_amdgcn_readfirstlane(claimed);  // uniform: in scalar registers
+  if (item < 0) return;
+  const int L = mha ? item : xcd_remap(item, P.n_items);
   const int e = mha ? 0 : L % P.R, t_ = mha ? L : L / P.R;
   const int g = mha ? t_ / P.t.nmajor : t_ % P.Hkv, rank = mha ? t_ % P.t.nmajor : t_ / P.Hkv;
   const int h = g * P.R + e;
@@ -361,9 +369,12 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
 // D = 256, whose K / V double buffer also fills 141 KB of LDS).
 constexpr int FWD_NB = 1;
 
-hipError_t launch_fwd(const AttnParams& P, int D, int n_items, hipStream_t stream) {
+hipError_t launch_fwd(AttnParams P, int D, int n_items, hipStream_t stream) {
   if (n_items <= 0) return hipSuccess;
-  auto run = [&](auto k, int nb) { hipLaunchKernelGGL(k, dim3(n_items), dim3(256 / nb), 0, stream, P); };
+  P.n_items = n_items;
+  if (P.queue) hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(64), 0, stream, P.queue);
+  const dim3 grid(P.queue ? claim_grid(n_items) : n_items);
+  auto run = [&](auto k, int nb) { hipLaunchKernelGGL(k, grid, dim3(256 / nb), 0, stream, P); };
   if (P.R == 1 && (P.m.mode == MODE_BLOCKS || P.t.uniform)) {
     if (D == 128) run(fwd_kernel<128, FWD_NB, true>, FWD_NB);
     else if (D == 256) run(fwd_kernel<256, 1, true>, 1);

@@ -49,8 +49,8 @@ struct AttnParams {
   float* dk_acc;      // dK/dV kernel with kv_splits > 1: fp32 [Tk, Hkv, D] sums of the column chunks
   float* dv_acc;
   int32_t kv_splits;  // dK/dV kernel: workgroups per key-tile column (1: each column in one workgroup)
-  int32_t* queue;     // dQ kernel: 8 item-claim counters (see claim_item), zero at launch
-  int32_t n_items;    // dQ kernel: work items of the launch
+  int32_t* queue;     // forward / dQ kernels: 8 item-claim counters (claim_item), zero at launch; or NULL
+  int32_t n_items;    // forward / dQ kernels: work items of the launch
   int64_t q_tok, q_head, k_tok, k_head, v_tok, v_head;
   int32_t Tq, Tk, Hq, Hkv;
   int32_t R;        // Hq / Hkv
@@ -322,7 +322,7 @@ struct TileLoader {
   }
 };
 
-// Work-item claim of the dQ kernel.  Items are numbered as in a grid
+// Work-item claim of the forward and dQ kernels.  Items are numbered as in a grid
 // of one workgroup per item, where the hardware runs workgroup b on XCD
 // b % 8; queue x holds the items b < n with b % 8 == x, in increasing order,
 // so that each XCD keeps the items (and the L2 sharing) it would have had.
@@ -344,7 +344,8 @@ __device__ __forceinline__ int claim_item(int32_t* queue, int n) {
     const int x = (home + k) & 7;
     const int len = (n - x + 7) >> 3;  // items x + 8p < n
     if (len <= 0) continue;
-    if (__hip_atomic_load(queue + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= len) continue;
+    // other queues are read first, so that empty ones cost no atomic
+    if (k > 0 && __hip_atomic_load(queue + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= len) continue;
     const int p = atomicAdd(queue + x, 1);
     if (p < len) return x + 8 * p;
   }
@@ -356,6 +357,13 @@ __device__ __forceinline__ int claim_item(int32_t* queue, int n) {
 // share finds workgroups to take over the slower XCDs' last items; the
 // workgroups left over find every queue empty and exit at once.
 inline int claim_grid(int n) { return n + n / 8 + 8; }
+
+// A kernel's 8 item-claim counters start at zero (a kernel rather than a
+// memset, so that the launches can be captured in a graph).  Static: each
+// source file that launches it has its own copy.
+static __global__ __launch_bounds__(64) void queue_reset_kernel(int32_t* q) {
+  if (threadIdx.x < 8) q[threadIdx.x] = 0;
+}
 
 // Block index remap so that 8 consecutive logical work items (the query
 // heads of one GQA group at one tile) land on the same XCD: workgroups are

@@ -382,8 +382,11 @@ extern "C" mad_status mad_ring_fwd(mad_ring* r, const void* q, const void* k, co
     if (e != hipSuccess) return hipf("mad_ring_fwd: staging", e);
     bf16* op = r->opart + (int64_t)i * qe;
     float* lp = r->lpart + (int64_t)i * le;
+    // the backward's workspace is idle during the forward and holds the
+    // forward kernel's item-claim counters (each step's forward runs on
+    // `stream` after the previous one)
     s = mad_attn_fwd(r->steps[i].plan, q, r->kst[slot], r->vst[slot], op, lp, r->C, r->C, r->Hq, r->Hkv, r->d,
-                     nullptr, scale, stream);
+                     nullptr, scale, r->ws, r->ws_bytes, stream);
     if (s != MAD_OK) return s;
     e = hipEventRecord(r->ev_done[slot], stream);
     if (e != hipSuccess) return hipf("mad_ring_fwd: order", e);

@@ -43,7 +43,8 @@ def gpu_attention(plan, q, k, v, do, scale, bwd=True, o_in=None, lse_in=None, fi
         return t if fill is None else t.fill_(fill)
     o = out_like((Tq, Hq, d), torch.bfloat16)
     lse = out_like((Hq, Tq), torch.float32)
-    mad.attn_fwd(plan, qd, kd, vd, o, lse, scale)
+    fws = torch.empty(mad.FWD_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)  # the forward claims its items
+    mad.attn_fwd(plan, qd, kd, vd, o, lse, scale, workspace=fws)
     out = {}
     if bwd:
         dod = do.to(dev)

@@ -129,7 +129,8 @@ def test_attention_argument_errors_launch_nothing():
     assert _status(e) == 1 and "phase" in str(e.value)
     assert mad.bwd_workspace_bytes(plan, T, T, 4, 2, 128) >= 4 * T * 4
     L = mad.lib()
-    assert L.mad_attn_fwd(None, None, None, None, None, None, 1, 1, 1, 1, 64, None, ctypes.c_float(1.0), None) == 1
+    assert L.mad_attn_fwd(None, None, None, None, None, None, 1, 1, 1, 1, 64, None, ctypes.c_float(1.0), None, 0,
+                          None) == 1
     assert b"plan is NULL" in L.mad_last_error()
 
 

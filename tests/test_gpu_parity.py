@@ -189,6 +189,35 @@ def test_rectangular_slices():
     _run_case(spec, plan, 4, 4, 128, seed=5)
 
 
+@pytest.mark.parametrize("pattern", ["CAUSAL", "FULL_DOCUMENT"])
+def test_forward_workspace_does_not_change_results(pattern):
+    """With a workspace the forward's workgroups claim their items from per-XCD queues (the grid holds more
+    workgroups than items); without one each takes a fixed item.  Each item is computed the same way
+    either way, so O and LSE are bit-identical, and both match the oracle."""
+    import torch
+    import mask_aware_dense_amd as mad
+    T, Hq, Hkv, d = 1100, 8, 2, 128
+    docs = {"doc_lens": (300, 512, 288)} if pattern == "FULL_DOCUMENT" else {}
+    spec = M.MaskSpec(pattern, T, T, **docs)
+    plan = _plan_for(spec).upload()
+    q, k, v = qkv(31, T, T, Hq, Hkv, d)
+    dev = torch.device("cuda", 0)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    fws = torch.empty(mad.FWD_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+    outs = []
+    for ws in (None, fws, fws):
+        o = torch.full((T, Hq, d), float("nan"), dtype=torch.bfloat16, device=dev)
+        lse = torch.full((Hq, T), float("nan"), dtype=torch.float32, device=dev)
+        mad.attn_fwd(plan, qd, kd, vd, o, lse, 1 / np.sqrt(d), workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), lse.cpu()))
+    for o, lse in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
+    O, L = A.attn_fwd(q, k, v, spec, 1 / np.sqrt(d))
+    _gpu.check_close("o", outs[1][0].float().numpy(), O, _gpu.TOL_FWD)
+    _gpu.check_lse(outs[1][1].numpy(), L)
+
+
 def test_strided_inputs_and_determinism():
     """q, k, v as views of one fused [T, Hq + 2 Hkv, d] tensor; forward repeats bit for bit."""
     import torch

@@ -23,7 +23,8 @@ def _run(plan, q, k, v, do, scale):
     plan.upload()
     o = torch.empty_like(q)
     lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
-    mad.attn_fwd(plan, q, k, v, o, lse, scale)
+    fws = torch.empty(mad.FWD_WORKSPACE_BYTES, dtype=torch.uint8, device=q.device)
+    mad.attn_fwd(plan, q, k, v, o, lse, scale, workspace=fws)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(max(mad.bwd_workspace_bytes(plan, Tq, Tk, Hq, Hkv, d), 256), dtype=torch.uint8, device=q.device)
     mad.attn_bwd(plan, q, k, v, o, do, lse, dq, dk, dv, ws, scale)
