@@ -298,8 +298,8 @@ void mad_plan_destroy(mad_plan* plan);
  * been compiled for (Tq, Tk), uploaded, and have n_groups dividing Hq.
  * ------------------------------------------------------------------------- */
 
-/* Device workspace of mad_attn_fwd (optional): 8 counters through which
- * the kernel's workgroups claim their work items. */
+/* Device workspace of mad_attn_fwd (optional): the counters through which
+ * the kernel's workgroups claim their work items (64 bytes used). */
 #define MAD_FWD_WORKSPACE_BYTES 256
 
 /* Forward: O = softmax(scale * Q K^T + mask) V and LSE (LongCA-bench

@@ -87,7 +87,7 @@ int device_cus() {
   return n;
 }
 
-// Workspace bytes of the dQ kernel's item-claim counters (8 used).
+// Workspace bytes of the dQ kernel's item-claim counters (64 used).
 constexpr size_t kQueueBytes = 256;
 
 // Workgroups per key-tile column of the dK/dV kernel.  The kernel runs one

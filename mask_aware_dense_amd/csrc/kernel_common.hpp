@@ -49,7 +49,7 @@ struct AttnParams {
   float* dk_acc;      // dK/dV kernel with kv_splits > 1: fp32 [Tk, Hkv, D] sums of the column chunks
   float* dv_acc;
   int32_t kv_splits;  // dK/dV kernel: workgroups per key-tile column (1: each column in one workgroup)
-  int32_t* queue;     // forward / dQ kernels: 8 item-claim counters (claim_item), zero at launch; or NULL
+  int32_t* queue;     // forward / dQ kernels: item-claim counters (claim_item, 64 bytes), zero at launch; or NULL
   int32_t n_items;    // forward / dQ kernels: work items of the launch
   int64_t q_tok, q_head, k_tok, k_head, v_tok, v_head;
   int32_t Tq, Tk, Hq, Hkv;
@@ -322,32 +322,41 @@ struct TileLoader {
   }
 };
 
-// Work-item claim of the forward and dQ kernels.  Items are numbered as in a grid
-// of one workgroup per item, where the hardware runs workgroup b on XCD
-// b % 8; queue x holds the items b < n with b % 8 == x, in increasing order,
-// so that each XCD keeps the items (and the L2 sharing) it would have had.
-// A workgroup takes the next item of its home queue (its own XCD's,
-// blockIdx.x % 8) and, once that is empty, of the other queues in turn.  The
-// XCDs finish identical shares of work at times that differ by 3-7%
-// (measured per workgroup on the real-time clock), so with a fixed share per
-// XCD the faster ones sit idle at the end; with the queues and a grid larger
-// than the item count (claim_grid) they take over the slower ones' last
-// (shortest) items: dQ 20.8 -> 20.3 ms at CAUSAL 32K GQA 64:8.  (The dK/dV
-// kernel's items, whole key-tile columns of up to a quarter of a CU's share,
-// are mostly already running when the fast XCDs run out; the claim gained
-// nothing there.)  Each queue hands out each of its items once.  Called by
-// one lane; the caller broadcasts the result.  Returns the item, or -1 when
-// every queue is empty.
+// Work-item claim of the forward and dQ kernels.  Items are numbered as in a
+// grid of one workgroup per item, where the hardware runs workgroup b on XCD
+// b % 8; queue x holds the items b < n with b % 8 == x, in increasing
+// (longest-first) order, so that each XCD keeps the items (and the L2
+// sharing) it would have had.  A workgroup takes the next item from the front
+// of its home queue (its own XCD's, blockIdx.x % 8) and, once that is empty,
+// from the back of the other queues in turn: their shortest items.  The XCDs
+// finish identical shares of work at times that differ by 3-7% (measured per
+// workgroup on the real-time clock), so with a fixed share per XCD the faster
+// ones sit idle at the end; with the queues and a grid larger than the item
+// count (claim_grid) they take over the slower ones' last items: dQ 20.8 ->
+// 20.3 ms at CAUSAL 32K GQA 64:8.  (The dK/dV kernel gained nothing from
+// either end; its items, whole key-tile columns, are long.)  Each queue is
+// one 64-bit counter, front count low and back count high; a claim succeeds
+// while front + back < the queue's length, so each item goes out once.
+// Called by one lane; the caller broadcasts the result.  Returns the item, or
+// -1 when every queue is empty.
 __device__ __forceinline__ int claim_item(int32_t* queue, int n) {
+  unsigned long long* q = reinterpret_cast<unsigned long long*>(queue);
   const int home = (int)(blockIdx.x & 7u);
   for (int k = 0; k < 8; ++k) {
     const int x = (home + k) & 7;
     const int len = (n - x + 7) >> 3;  // items x + 8p < n
     if (len <= 0) continue;
-    // other queues are read first, so that empty ones cost no atomic
-    if (k > 0 && __hip_atomic_load(queue + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= len) continue;
-    const int p = atomicAdd(queue + x, 1);
-    if (p < len) return x + 8 * p;
+    if (k == 0) {  // own queue: from the front (longest first)
+      const unsigned long long old = atomicAdd(q + x, 1ull);
+      const int f = (int)(uint32_t)old, b = (int)(old >> 32);
+      if (f + b < len) return x + 8 * f;
+    } else {       // another XCD's: from the back (its shortest items); read first, so that empty ones cost no atomic
+      const unsigned long long cur = __hip_atomic_load(q + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((int)(uint32_t)cur + (int)(cur >> 32) >= len) continue;
+      const unsigned long long old = atomicAdd(q + x, 1ull << 32);
+      const int f = (int)(uint32_t)old, b = (int)(old >> 32);
+      if (f + b < len) return x + 8 * (len - 1 - b);
+    }
   }
   return -1;
 }
@@ -358,11 +367,11 @@ __device__ __forceinline__ int claim_item(int32_t* queue, int n) {
 // workgroups left over find every queue empty and exit at once.
 inline int claim_grid(int n) { return n + n / 8 + 8; }
 
-// A kernel's 8 item-claim counters start at zero (a kernel rather than a
+// A kernel's item-claim counters (64 bytes) start at zero (a kernel rather than a
 // memset, so that the launches can be captured in a graph).  Static: each
 // source file that launches it has its own copy.
 static __global__ __launch_bounds__(64) void queue_reset_kernel(int32_t* q) {
-  if (threadIdx.x < 8) q[threadIdx.x] = 0;
+  if (threadIdx.x < 16) q[threadIdx.x] = 0;  // 8 queues x (front, back)
 }
 
 // Block index remap so that 8 consecutive logical work items (the query
