@@ -218,6 +218,26 @@ def test_forward_workspace_does_not_change_results(pattern):
     _gpu.check_lse(outs[1][1].numpy(), L)
 
 
+def test_forward_workspace_errors():
+    """A forward workspace shorter than FWD_WORKSPACE_BYTES is refused (MAD_ERR_INVALID) and so is one not
+    256-byte aligned (MAD_ERR_UNSUPPORTED), before anything is launched: o and lse keep their contents."""
+    import torch
+    import mask_aware_dense_amd as mad
+    T, Hq, Hkv, d = 256, 4, 2, 64
+    plan = mad.mask_compile(mad.mask_slices("CAUSAL", T), T, T).upload()
+    dev = torch.device("cuda", 0)
+    q, k, v = (x.to(dev) for x in qkv(3, T, T, Hq, Hkv, d))
+    o = torch.full((T, Hq, d), 7.0, dtype=torch.bfloat16, device=dev)
+    lse = torch.full((Hq, T), 7.0, dtype=torch.float32, device=dev)
+    buf = torch.empty(2 * mad.FWD_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+    for ws, status in ((buf[:128], 1), (buf[16:16 + mad.FWD_WORKSPACE_BYTES], 2)):
+        with pytest.raises(mad.MadError) as e:
+            mad.attn_fwd(plan, q, k, v, o, lse, 0.125, workspace=ws)
+        assert e.value.status == status, str(e.value)
+    torch.cuda.synchronize()
+    assert bool((o == 7.0).all()) and bool((lse == 7.0).all())
+
+
 def test_strided_inputs_and_determinism():
     """q, k, v as views of one fused [T, Hq + 2 Hkv, d] tensor; forward repeats bit for bit."""
     import torch
