@@ -365,7 +365,12 @@ __device__ __forceinline__ int claim_item(int32_t* queue, int n) {
 // plus an eighth more, so that an XCD running up to 12.5% faster than its
 // share finds workgroups to take over the slower XCDs' last items; the
 // workgroups left over find every queue empty and exit at once.
-inline int claim_grid(int n) { return n + n / 8 + 8; }
+// (Clamped to the int range: any grid of at least n workgroups still runs
+// every item.)
+inline int claim_grid(int n) {
+  const int64_t g = (int64_t)n + n / 8 + 8;
+  return g > INT32_MAX ? INT32_MAX : (int)g;
+}
 
 // A kernel's item-claim counters (64 bytes) start at zero (a kernel rather than a
 // memset, so that the launches can be captured in a graph).  Static: each
