@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void delta_kernel(const AttnParams P) {
 // operands and the dQ accumulator take 256 registers per lane (421 in all).
 // HM: the head-major item order (MHA masks whose tiles carry even work).
 template <int D, bool HM>
-__global__ __launch_bounds__(256, D == 256 ? 1 : 2) void dq_kernel(const AttnParams P) {
+__global__ __launch_bounds__(256, D == 256 ? 1 : D == 64 ? 3 : 2) void dq_kernel(const AttnParams P) {
   constexpr int BM = BM0, BN = BN0, NKS = D / 16, NDB = D / 32;
   constexpr int KRS = tile_rs<D, TILE_MIXED>(), KT = tile_elems<D, TILE_MIXED>();
   constexpr int VRS = tile_rs<D, TILE_ROWS>(), VT = tile_elems<D, TILE_ROWS>();
