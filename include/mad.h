@@ -266,8 +266,8 @@ mad_status mad_plan_device_bytes(const mad_plan* plan, size_t* bytes);
 /* Plan shape: Tq, Tk, number of mask groups, and tile sizes (BM query rows x
  * BN keys) with tile-grid size of tiling `which`: 128 x 64 for tiling 0
  * (forward, dQ); 64 x 128 for tiling 1 (dK/dV), or 64 x 64 for block-sparse
- * plans whose interior key-block edges are all multiples of 64 but not all
- * of 128.  Any out pointer may be NULL. */
+ * plans whose interior key-block edges are not all multiples of 128 (64-token
+ * or variable blocks).  Any out pointer may be NULL. */
 mad_status mad_plan_info(const mad_plan* plan, int32_t which, int32_t* Tq, int32_t* Tk,
                          int32_t* n_groups, int32_t* BM, int32_t* BN, int32_t* n_qt,
                          int32_t* n_kt);

@@ -8,7 +8,8 @@
 //   dV_j  = sum_h sum_i P_ij dO_i,   dK_j = scale sum_h sum_i dS_ij q_i
 //
 // Work decomposition: one workgroup per (KV head, 128-key tile), four waves
-// of 32 keys (per 64-key tile, two waves, for plans of 64-token key blocks).
+// of 32 keys (per 64-key tile, two waves, for block-sparse plans of smaller
+// key blocks).
 // K and V of the wave's keys stay in registers as MFMA operands.
 // The workgroup walks, for each query head of the group, the key tile's list
 // of non-EMPTY 64-row query tiles; the Q / dO tiles and their -LSE/scale and
@@ -136,8 +137,8 @@ struct KvWalk {
 };
 
 // NW waves of 32 keys: a 128-key tile (NW = 4, one workgroup per CU) or,
-// for block-sparse plans of 64-token key blocks, a 64-key tile (NW = 2, two
-// workgroups per CU).
+// for block-sparse plans of smaller key blocks (64-token or variable), a
+// 64-key tile (NW = 2, two workgroups per CU).
 // HM: the head-major item order (MHA masks whose columns carry even work).
 template <int D, int NW, bool HM>
 __global__ __launch_bounds__(64 * NW) void dkdv_kernel(const AttnParams P) {

@@ -5,7 +5,7 @@
 //   tiling 0 (forward and dQ kernels): BM0 query rows x BN0 keys, visited as
 //            per-query-tile lists of key tiles (CSR);
 //   tiling 1 (dK/dV kernel):           BM1 query rows x BN1 keys (BN1_FINE
-//            for block-sparse masks of 64-token key blocks), visited as
+//            for block-sparse masks of smaller key blocks), visited as
 //            per-key-tile lists of query tiles (CSC).
 // Every tile is EMPTY (never visited), FULL (no mask arithmetic) or PARTIAL
 // (per-element mask), judged on its in-range elements only.  The O(#tiles)
@@ -34,20 +34,17 @@ namespace mad {
 // these.
 constexpr int BM0 = 128, BN0 = 64;   // forward / dQ
 constexpr int BM1 = 64, BN1 = 128;   // dK / dV
-// dK / dV key tile of block-sparse plans whose key-block edges are all
-// multiples of 64 but not all of 128 (64-token blocks): one key block per
-// tile, so no tile leaves half its waves without keys (a 128-key tile keeps
-// only one of its two blocks in most visited tiles); its workgroup has two
-// waves, and two workgroups share a CU.
+// dK / dV key tile of block-sparse plans whose interior key-block edges are
+// not all multiples of 128 (64-token blocks, variable block sizes): a
+// 128-key tile would keep only part of its keys in most visited tiles and
+// leave waves without work (with 64-token blocks, one of its two blocks);
+// the 64-key tile's workgroup has two waves, and two workgroups share a CU.
 constexpr int BN1_FINE = 64;
 // The dK / dV key-tile width for a block-sparse plan with these key edges.
 inline int dkdv_tile_keys(const int32_t* k_edges, int32_t n_kb) {
-  bool all64 = true, all128 = true;
-  for (int32_t b = 1; b < n_kb; ++b) {  // interior edges (the last one is Tk)
-    all64 &= k_edges[b] % 64 == 0;
-    all128 &= k_edges[b] % 128 == 0;
-  }
-  return (n_kb > 1 && all64 && !all128) ? BN1_FINE : BN1;
+  bool all128 = true;
+  for (int32_t b = 1; b < n_kb; ++b) all128 &= k_edges[b] % 128 == 0;  // interior edges (the last one is Tk)
+  return (n_kb > 1 && !all128) ? BN1_FINE : BN1;
 }
 
 enum MaskMode : int32_t { MODE_SLICES = 0, MODE_BLOCKS = 1 };

@@ -20,11 +20,11 @@ TILINGS = {0: (128, 64), 1: (64, 128)}
 
 def _tiling(spec, w):
     """Tile shape of tiling w: the dK/dV tiling of a block-sparse plan whose interior key-block edges
-    are all multiples of 64 but not all of 128 (64-token blocks) has 64-key tiles."""
+    are not all multiples of 128 (64-token blocks, variable blocks) has 64-key tiles."""
     BM, BN = TILINGS[w]
     if w == 1 and spec.k_edges is not None:
         inner = np.asarray(spec.k_edges[1:-1])
-        if inner.size and np.all(inner % 64 == 0) and not np.all(inner % 128 == 0):
+        if inner.size and not np.all(inner % 128 == 0):
             BN = 64
     return BM, BN
 
