@@ -9,8 +9,9 @@
 //   dK_j  = scale * sum_{h in group} sum_i dS_ij q_i,  dV_j = sum_{h in group} sum_i P_ij dO_i   (dK/dV kernel)
 // The pages single out the backward pass as the common bottleneck (section
 // 3.2, the notes' key findings).  Here it is split into three launches with
-// no atomics: a streaming delta pre-pass, a dK/dV kernel that owns a key
-// tile and walks the query tiles of its per-key-tile list for every query
+// no atomic adds into the gradients (but for dK/dV columns cut between
+// workgroups, below): a streaming delta pre-pass, a dK/dV kernel that owns a
+// key tile and walks the query tiles of its per-key-tile list for every query
 // head of its GQA group, and a dQ kernel that owns a query tile and walks its
 // key-tile list (the forward's tiling).  Both recompute P from LSE.
 //
@@ -19,7 +20,9 @@
 //   rows that have no allowed key or lie past Tq -- so their P is exactly 0.
 // Both are stored negated so that the dK/dV kernel can start its score and
 // dP accumulators from them: P = exp2(scale log2e (q.k + nlse)) and
-// dS = P (dP + ndelta).
+// dS = P (dP + ndelta).  The last 256 bytes of the required workspace size
+// hold the dQ launch's per-XCD work-claim counters (cleared by a kernel
+// before it).
 #include "kernel_common.hpp"
 
 namespace mad {

@@ -6,13 +6,15 @@
 // start from (section 1), under a compiled mask.  A row with no allowed key
 // gets O = 0, LSE = -inf.
 //
-// Work decomposition: one workgroup per (query head, 128-row query tile), four
-// wave64s of 32 rows each (two workgroups per CU at head dim 64 / 128, so two
-// waves share each SIMD).  The workgroup walks the query tile's list of
-// non-EMPTY 64-key tiles.  K and V tiles reach LDS by direct global->LDS
-// loads into a double buffer: the loads of tile t+1 are issued right after
-// the barrier that opens tile t, so they overlap tile t's arithmetic and no
-// registers are spent on staging.  Per key tile each wave
+// Work decomposition: one work item per (query head, 128-row query tile),
+// run by one workgroup of four wave64s of 32 rows each (two workgroups per
+// CU at head dim 128, three at 64 and one at 256).  With a caller workspace
+// the workgroups claim their items from per-XCD queues (claim_item);
+// without one, workgroup b runs item b.  The workgroup walks the query
+// tile's list of non-EMPTY 64-key tiles.  K and V tiles reach LDS by direct
+// global->LDS loads into a double buffer: the loads of tile t+1 are issued
+// right after the barrier that opens tile t, so they overlap tile t's
+// arithmetic and no registers are spent on staging.  Per key tile each wave
 //   1. forms S^T = K Q^T (keys x queries) with bf16 MFMA; each lane then holds
 //      one query row, so the row max and row sum stay in the lane (plus one
 //      permlane32 swap with the other half-wave);
