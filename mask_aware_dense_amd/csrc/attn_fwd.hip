@@ -20,8 +20,9 @@
 //      permlane32 swap with the other half-wave);
 //   2. masks PARTIAL tiles (and the ragged last key tile) with -inf;
 //   3. updates the online softmax in the exp2 domain against a lagging
-//      reference max that moves (with a rescale of the accumulator) only when
-//      a row's max grows by more than 2^8;
+//      reference max: P is formed first, and the block's max is taken (the
+//      reference moved, the accumulator rescaled and P formed again) only
+//      when a lane's block sum of P exceeds 2^8 or a row has no reference;
 //   4. accumulates O^T += V^T P^T with P^T taken straight from registers as
 //      the MFMA B operand and V^T read transposed from LDS.
 #include "kernel_common.hpp"
@@ -38,9 +39,9 @@ namespace mad {
 #endif
 // HM: the head-major item order (MHA masks whose tiles carry even work).
 template <int D, int NB, bool HM>
-__global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
-  // Score steps of the next key block issued before a block's max is taken
-  // (stage B) and P V steps issued before the next block's max (stage C).
+__global__ __launch_bounds__(256 / NB, D == 64 ? 3 : 1) void fwd_kernel(const AttnParams P) {
+  // Score steps of the next key block issued before a block's softmax starts
+  // (stage B) and P V steps issued before the next block's softmax (stage C).
   constexpr int PRE_B = FWD_PRE_B < D / 16 - 1 ? FWD_PRE_B : D / 16 - 1;
   constexpr int PRE_C = FWD_PRE_C < D / 16 - 1 ? FWD_PRE_C : D / 16 - 1;
   constexpr int BM = BM0, BN = BN0, NKS = D / 16, NDB = D / 32, NW = 4 / NB;
@@ -118,6 +119,7 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[db][b] = f32x16{};
   float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
+  float muse[2] = {0.f, 0.f};  // the reference P is formed against (0 while mrow is -inf)
 
   for (int it = beg; it < end; ++it) {
     const int buf = (it - beg) & 1;
@@ -208,38 +210,54 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
       for (int b = 0; b < NB; ++b) acc[db][b] = mfma32(vr[st % 3], pb[kb][t2][b], acc[db][b]);
     };
     // Online softmax in the exp2 domain against a lagging reference max per
-    // row: p = exp2(s c - m_ref); m_ref moves (and O, l are rescaled by
-    // exp2(m_old - m_new)) only when a key block's max exceeds it by more
-    // than RESCALE_SLACK, so p < 2^RESCALE_SLACK and rescales are rare.  The
+    // row: p = exp2(s c - m_ref) is formed against the current reference
+    // first.  Only when some lane's sum of its block's p exceeds SUM_LIMIT =
+    // 2^8 (so that some p may), or some row of the wave has no reference yet
+    // (mrow = -inf: p was formed against 0 and may have underflowed), does
+    // the wave take the block's max: m_ref moves to it if larger, O and l are
+    // rescaled by exp2(m_old - m_new) and the block's p are formed again.
+    // Otherwise every p is at most 2^8 and no max is taken at all.  The
     // result is exact: O and l share the reference and LSE = m_ref + log2 l.
-    constexpr float RESCALE_SLACK = 8.f;
-    float muse[2];
-    auto block_max = [&](int kb, float* tmax) {
-      bool need = false;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][b][r]);
-        tmax[b] = pair_max(mx) * P.scale_log2;
-        need |= tmax[b] > mrow[b] + RESCALE_SLACK;
-      }
-      return __ballot(need) != 0ull;
-    };
-    auto set_use = [&]() {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) muse[b] = (mrow[b] == -INFINITY) ? 0.f : mrow[b];
-    };
+    constexpr float SUM_LIMIT = 256.f;
+    constexpr int NE = 16 * NB;  // softmax elements per key block and lane
+    float tsum[2][NB];           // per-lane sums of the block's p
     // P = exp2(s c - m) for elements e, e + 1 of key block kb (e = 16 b + r),
-    // summed into l and written as bf16 into the P^T operand.
+    // summed into tsum and written as bf16 into the P^T operand.
     auto softmax2 = [&](int kb, int e) {
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int b = (e + x) >> 4, r = (e + x) & 15;
         const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][b][r], P.scale_log2, -muse[b]));
-        lrow[b] += pv;
+        tsum[kb][b] = r == 0 ? pv : tsum[kb][b] + pv;
         pb[kb][r >> 3][b][r & 7] = (bf16)pv;
       }
+    };
+    auto needs_max = [&](int kb) {
+      bool need = false;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) need |= !(tsum[kb][b] <= SUM_LIMIT) || mrow[b] == -INFINITY;
+      return __ballot(need) != 0ull;
+    };
+    // The rare path: take block kb's max, move the reference, rescale O (all
+    // products so far) and l, and form the block's p again.
+    auto move_reference = [&](int kb) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][b][r]);
+        const float mnew = fmaxf(mrow[b], pair_max(mx) * P.scale_log2);
+        const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrow[b] - mnew);
+        mrow[b] = mnew;
+        muse[b] = (mnew == -INFINITY) ? 0.f : mnew;
+        lrow[b] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][b][r] *= alpha;
+      }
+#pragma unroll
+      for (int e = 0; e < NE; e += 2) softmax2(kb, e);
     };
 
     ldk(0);
@@ -253,9 +271,9 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
       __builtin_amdgcn_sched_barrier(0);
     }
     // Stage B: scores of key block 1 under the softmax of block 0.  Its first
-    // PRE_B steps are issued before block 0's max is taken, so the matrix
-    // cores stay busy while the vector unit waits for block 0's last products
-    // and reduces them.
+    // PRE_B steps are issued before block 0's softmax starts, so the matrix
+    // cores stay busy while the vector unit waits for block 0's last
+    // products.
 #pragma unroll
     for (int st = NKS; st < NKS + PRE_B; ++st) {
       if (st + 2 < 2 * NKS) ldk(st + 2);
@@ -263,25 +281,7 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
       s_step(st);
       __builtin_amdgcn_sched_barrier(0);
     }
-    {
-      float tmax[2];
-      if (__builtin_expect(masked, 0)) apply_mask(0);
-      if (block_max(0, tmax)) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const float mnew = fmaxf(mrow[b], tmax[b]);
-          const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrow[b] - mnew);
-          mrow[b] = mnew;
-          lrow[b] *= alpha;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[db][b][r] *= alpha;
-        }
-      }
-      set_use();
-    }
-    constexpr int NE = 16 * NB;  // softmax elements per key block and lane
+    if (__builtin_expect(masked, 0)) apply_mask(0);
     constexpr int RB = NKS - PRE_B;                      // remaining stage-B steps
     constexpr int EB = 2 * ((NE / 2 + RB - 1) / RB);     // block-0 elements per remaining stage-B step (even)
 #pragma unroll
@@ -293,32 +293,20 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
       for (int e = (st - NKS - PRE_B) * EB; e < (st - NKS - PRE_B + 1) * EB && e < NE; e += 2) softmax2(0, e);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // Stage C: O^T += V^T P^T for key block 0 under the softmax of block 1.
-    // Block 1's reference is settled first; the accumulator's rescale (which
-    // must include block 0's products) waits until they are in.
+    if (__builtin_expect(needs_max(0), 0)) move_reference(0);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) lrow[b] += tsum[0][b];
+    __builtin_amdgcn_sched_barrier(0);
+    // Stage C: O^T += V^T P^T for key block 0 under the softmax of block 1
+    // (whose reference check, and any rescale of the accumulator, waits until
+    // block 0's products are in).
 #pragma unroll
     for (int st = 0; st < PRE_C; ++st) {
       ldv(st + 2);
       pv_step(st);
       __builtin_amdgcn_sched_barrier(0);
     }
-    float alpha1[2] = {1.f, 1.f};
-    bool resc1;
-    {
-      float tmax[2];
-      if (__builtin_expect(masked, 0)) apply_mask(1);
-      resc1 = block_max(1, tmax);
-      if (resc1) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const float mnew = fmaxf(mrow[b], tmax[b]);
-          alpha1[b] = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrow[b] - mnew);
-          mrow[b] = mnew;
-          lrow[b] *= alpha1[b];
-        }
-      }
-      set_use();
-    }
+    if (__builtin_expect(masked, 0)) apply_mask(1);
     constexpr int RC = 2 * NDB - PRE_C;                  // remaining stage-C steps
     constexpr int EC = 2 * ((NE / 2 + RC - 1) / RC);     // block-1 elements per remaining stage-C step (even)
 #pragma unroll
@@ -329,14 +317,10 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
       for (int e = (st - PRE_C) * EC; e < (st - PRE_C + 1) * EC && e < NE; e += 2) softmax2(1, e);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (resc1) {
+    if (__builtin_expect(needs_max(1), 0)) move_reference(1);
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][b][r] *= alpha1[b];
-    }
+    for (int b = 0; b < NB; ++b) lrow[b] += tsum[1][b];
+    __builtin_amdgcn_sched_barrier(0);
     // Stage D: O^T += V^T P^T for key block 1.
 #pragma unroll
     for (int st = 2 * NDB; st < 4 * NDB; ++st) {
@@ -367,7 +351,7 @@ __global__ __launch_bounds__(256 / NB) void fwd_kernel(const AttnParams P) {
   }
 }
 
-// 4 waves of 32 rows: 220 registers at D = 128, two waves per SIMD (one at
+// 4 waves of 32 rows: 237 registers at D = 128, two waves per SIMD (one at
 // D = 256, whose K / V double buffer also fills 141 KB of LDS).
 constexpr int FWD_NB = 1;
 

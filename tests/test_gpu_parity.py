@@ -129,6 +129,39 @@ def test_ring_step_d256():
     _run_case(spec, _plan_for(spec), 8, 2, 256, seed=77)
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("pattern", ["FULL", "CAUSAL"])
+def test_forward_extreme_score_ranges(pattern, d):
+    """Score ranges that the forward's lagging softmax reference must follow, one kind per query
+    head: rising ramps along the keys, steep (300 log2 units per 64-key tile, so that p formed
+    against the previous tile's reference overflows fp32) or mild (5 per tile, so that lane sums
+    of p pass 2^8 without overflowing), falling ramps, and rows whose every score lies about 400
+    log2 units below zero (p formed against a reference of 0 underflows to 0).  The oracle's
+    softmax subtracts each row's exact max, so O and LSE are compared as in every other case.
+    Forward only (the backward reads the forward's LSE and never forms a running max)."""
+    torch = _gpu.torch_mod()
+    T, Hq, Hkv = 1000, 8, 2
+    q, k, v = qkv(17, T, T, Hq, Hkv, d)
+    q, k = q.float(), k.float()
+    k[:, :, 0] = (torch.arange(T, dtype=torch.float32) / 64)[:, None]  # one unit per 64-key tile
+    k[:, :, 1] = 4.0
+    unit = np.sqrt(d) / np.log2(np.e)  # a Q component of `unit` per unit of K adds one log2 unit
+    ramp = [0, 300, 5, 0, -300, 5, 0, -5]       # log2 units per 64-key tile
+    offset = [0, 0, 0, -400, 0, -400, 0, 0]     # log2 units on every score of the row
+    for h in range(Hq):
+        q[:, h, 0] = ramp[h] * unit
+        q[:, h, 1] = offset[h] / 4 * unit
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    spec = M.MaskSpec(pattern, T, T)
+    scale = 1.0 / np.sqrt(d)
+    print(f"case extreme scores {pattern} T={T} Hq={Hq} Hkv={Hkv} d={d}", flush=True)
+    got = _gpu.gpu_attention(_plan_for(spec), q, k, v, None, scale, bwd=False)
+    O, L = A.attn_fwd(q, k, v, spec, scale)
+    assert np.all(np.isfinite(L)) and L.max() > 2000 and L.min() < -200  # the ranges are as intended
+    _gpu.check_close("o", got["o"], O, _gpu.TOL_FWD)
+    _gpu.check_lse(got["lse"], L)
+
+
 @pytest.mark.parametrize("d", [64, 256])
 @pytest.mark.parametrize("T", [1, 17, 65, 129])
 def test_tiny_and_ragged(T, d):
