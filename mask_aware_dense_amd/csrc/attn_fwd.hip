@@ -299,7 +299,10 @@ __global__ __launch_bounds__(256 / NB, D == 64 ? 3 : 1) void fwd_kernel(const At
     __builtin_amdgcn_sched_barrier(0);
     // Stage C: O^T += V^T P^T for key block 0 under the softmax of block 1
     // (whose reference check, and any rescale of the accumulator, waits until
-    // block 0's products are in).
+    // block 0's products are in).  The wave runs it, up to block 1's check,
+    // at raised issue priority: its exponentials then go ahead of the other
+    // wave on the SIMD, whose stage A or D is matrix work alone.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int st = 0; st < PRE_C; ++st) {
       ldv(st + 2);
@@ -321,6 +324,7 @@ __global__ __launch_bounds__(256 / NB, D == 64 ? 3 : 1) void fwd_kernel(const At
 #pragma unroll
     for (int b = 0; b < NB; ++b) lrow[b] += tsum[1][b];
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
     // Stage D: O^T += V^T P^T for key block 1.
 #pragma unroll
     for (int st = 2 * NDB; st < 4 * NDB; ++st) {
